@@ -1,0 +1,170 @@
+/*
+ * mla.h -- C ABI of the chunk-causal multi-head latent attention library
+ * (libmla_hip.so, HIP kernels for AMD gfx950 / MI355X).
+ *
+ * What is computed.  VideoMLA (arXiv abstract on the mlsanity.com paper page;
+ * atlas.scime.ai summary, "Approach") replaces per-head keys and values with
+ * one low-rank content latent shared by all heads plus one head-shared,
+ * decoupled 3D-RoPE positional key.  Each cached token therefore keeps the
+ * row [c || k_R] of d_c + d_r scalars (224 at d_c = 192, d_r = 32, against
+ * 3072 for 12 heads x 128 of dense K and V; atlas summary, "Key results").
+ * Scores and up-projections follow multi-head latent attention as introduced
+ * by DeepSeek-V2 (listed under "Builds on" on both VideoMLA pages):
+ *
+ *   append   c = W_DKV x,  k_R = RoPE3D(t,h,w) (W_KR x),  row = bf16([c || k_R])
+ *   attend   s(i,h,j) = scale * ( q_h . (W_UK[h] c_j) + RoPE3D(p_i) q_r,h . k_R,j )
+ *            O(i,h)   = sum_j softmax_j(s) W_UV[h] c_j
+ * for a chunk of queries that sees every cached chunk and itself
+ * (chunk-causal, bidirectional inside the chunk: atlas summary, first
+ * paragraph).  The library evaluates attention in the absorbed form:
+ *   q~ = [scale*log2(e) * W_UK[h]^T q_h || scale*log2(e) * RoPE3D(p_i) q_r,h]
+ *   L  = softmax2(q~ . [c || k_R]) c      (fp32, over all visible keys)
+ *   O  = W_UV[h] L
+ * which is the same function up to rounding.
+ *
+ * Conventions for every entry point.
+ *   - Pointers marked "device" are device memory owned by the caller; the
+ *     library never allocates, frees or retains them beyond the enqueued work.
+ *   - Tensors are dense row-major with the shapes given, 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued asynchronously; nothing here synchronizes the device unless
+ *     the environment variable MLA_SYNC_CHECK=1 is set, in which case each
+ *     launch is followed by a stream synchronize and device faults are
+ *     reported as MLA_ERR_HIP.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     any error nothing is enqueued and a negative mla_status is returned.
+ *     mla_last_error() gives a human-readable reason (thread-local).
+ *   - The library keeps no global mutable state apart from a per-device cache
+ *     of the compute-unit count; calls are thread-safe.  Calls that share a
+ *     workspace must be ordered on one stream.
+ *   - dtype MLA_BF16 means every floating-point input of the call is bfloat16;
+ *     MLA_F32 means every one is float32.  Positions are always int32.
+ *
+ * Weight layouts ("out x in", as in DeepSeek-V2's W^{DKV}, W^{KR}, W^{UK},
+ * W^{UV}):
+ *   w_dkv [d_c, d_model]   w_kr [d_r, d_model]
+ *   w_uk  [H, d_h, d_c]    w_uv [H, d_h, d_c]
+ * Cache layout: cache[b][slot][0 .. d_c)      = c  of the token in that slot
+ *               cache[b][slot][d_c .. d_c+d_r) = k_R (already rotated)
+ * i.e. [B, capacity, d_c + d_r], 2*(d_c+d_r) bytes per slot in bf16.
+ *
+ * 3D-RoPE reading (the pages name 3D-RoPE but give no formula): the d_r
+ * vector is split into contiguous blocks of widths rope_t, rope_h, rope_w
+ * (even, summing to d_r); inside a block of width d_a the adjacent pair
+ * (2i, 2i+1) is rotated by angle p_a * rope_theta^(-2i/d_a), with
+ * p = (t, h, w) the token's latent frame index, row and column.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size, out-of-range offset   */
+  MLA_ERR_UNSUPPORTED = -2,  /* shape or dtype outside what the kernels are built for     */
+  MLA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than the required size       */
+  MLA_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed                */
+} mla_status;
+
+typedef enum mla_dtype { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
+
+/* Problem dimensions shared by all calls.  Supported: head_dim = 128,
+ * d_c in {64, 128, 192, 256}, d_r = 32, rope_t + rope_h + rope_w = d_r with
+ * each even, batch >= 1, n_heads >= 1, rope_theta > 0.
+ * Wan2.1-1.3B shape: {1, 12, 128, 192, 32, 8, 12, 12, 1e4}. */
+typedef struct mla_dims {
+  int32_t batch;
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t d_c;
+  int32_t d_r;
+  int32_t rope_t, rope_h, rope_w;
+  double rope_theta;
+} mla_dims;
+
+/* Cache append (latent down-projection + rotated positional key).
+ *   x        device [B, n_new, d_model]   hidden states of the new tokens
+ *   w_dkv    device [d_c, d_model]        latent down-projection
+ *   w_kr     device [d_r, d_model]        positional-key projection
+ *   pos_thw  device int32 [n_new, 3]      (t, h, w) of each new token (shared by the batch)
+ *   cache    device [B, cache_capacity, d_c + d_r]; slots write_offset ..
+ *            write_offset + n_new - 1 of every sample are overwritten, all
+ *            other slots are untouched.
+ * Each output value is accumulated in fp32 from the dtype inputs, rotated in
+ * fp32 with fp64-evaluated angles, and rounded once (to nearest even when the
+ * dtype is bf16).  Requires d_model % 32 == 0 (bf16), n_new >= 0,
+ * 0 <= write_offset, write_offset + n_new <= cache_capacity.  n_new == 0 is a
+ * no-op returning MLA_OK. */
+int32_t mla_cache_append(const mla_dims* dims, int32_t dtype,
+                         const void* x, int32_t d_model, int32_t n_new,
+                         const void* w_dkv, const void* w_kr,
+                         const int32_t* pos_thw,
+                         void* cache, int32_t cache_capacity, int32_t write_offset,
+                         void* stream);
+
+/* Bytes of device workspace mla_chunk_attend (and its three steps) needs for
+ * these sizes; negative mla_status on invalid arguments. */
+int64_t mla_chunk_attend_workspace_bytes(const mla_dims* dims, int32_t dtype,
+                                         int32_t n_q, int32_t n_k);
+
+/* One chunk step: absorb, attend, up-project (the three calls below, in order).
+ *   q        device [B, n_q, H, d_h]     content queries of the current chunk
+ *   q_r      device [B, n_q, H, d_r]     positional queries (rotated here)
+ *   q_pos    device int32 [n_q, 3]       (t, h, w) of each query token
+ *   w_uk, w_uv device [H, d_h, d_c]
+ *   cache    device [B, cache_capacity, d_c + d_r]; keys are slots 0 .. n_k-1
+ *            (all cached chunks plus the current chunk, already appended)
+ *   softmax_scale  the score scale (e.g. 1/sqrt(d_h + d_r))
+ *   out      device [B, n_q, H, d_h] of out_dtype
+ *   workspace device, at least mla_chunk_attend_workspace_bytes(...) bytes;
+ *            its contents on entry are irrelevant and on exit unspecified.
+ * Requires 1 <= n_q <= n_k <= cache_capacity. */
+int32_t mla_chunk_attend(const mla_dims* dims, int32_t in_dtype, int32_t out_dtype,
+                         const void* q, const void* q_r, const int32_t* q_pos, int32_t n_q,
+                         const void* w_uk, const void* w_uv,
+                         const void* cache, int32_t cache_capacity, int32_t n_k,
+                         float softmax_scale, void* out,
+                         void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Step 1 of mla_chunk_attend: writes the absorbed, pre-scaled queries q~
+ * (the content part W_UK[h]^T q_h and the rotated positional part, both
+ * multiplied by softmax_scale*log2(e), rounded once to the dtype) into the
+ * workspace.  Arguments as for mla_chunk_attend. */
+int32_t mla_query_absorb(const mla_dims* dims, int32_t dtype,
+                         const void* q, const void* q_r, const int32_t* q_pos, int32_t n_q,
+                         const void* w_uk, float softmax_scale, int32_t n_k,
+                         void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Step 2: fused score / online-softmax / P.c over all n_k keys for every
+ * (batch, query, head) row, leaving fp32 partial softmax states in the
+ * workspace.  Requires step 1 to have been enqueued with the same sizes. */
+int32_t mla_latent_attend(const mla_dims* dims, int32_t dtype,
+                          const void* cache, int32_t cache_capacity, int32_t n_q, int32_t n_k,
+                          void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Step 3: merges the partial softmax states of each row into L (fp32) and
+ * writes out = W_UV[h] L in out_dtype.  Requires steps 1 and 2. */
+int32_t mla_value_upproj(const mla_dims* dims, int32_t dtype, int32_t out_dtype,
+                         int32_t n_q, int32_t n_k, const void* w_uv, void* out,
+                         void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* mla_status_string(int32_t status);
+
+/* Reason for the last non-OK status returned on the calling thread. */
+const char* mla_last_error(void);
+
+/* Library version and the gfx target it was built for, e.g. "0.1.0 gfx950". */
+const char* mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,243 @@
+// C ABI of the latent-attention library: argument validation (host only,
+// nothing is enqueued on error), workspace planning and kernel dispatch.
+// Declarations and contracts: include/mla.h.
+#include "mla.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "mla_common.h"
+#include "mla_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool sync_check() {
+  static const bool on = [] {
+    const char* v = getenv("MLA_SYNC_CHECK");
+    return v != nullptr && v[0] == '1';
+  }();
+  return on;
+}
+
+int32_t finish(hipError_t launched, hipStream_t s, const char* what) {
+  if (launched != hipSuccess)
+    return fail(MLA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(launched));
+  if (sync_check()) {
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: kernel failed: %s", what, hipGetErrorString(e));
+  }
+  return MLA_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int32_t check_dims(const mla_dims* d) {
+  if (d == nullptr) return fail(MLA_ERR_INVALID_ARG, "dims is null");
+  if (d->batch < 1 || d->n_heads < 1) return fail(MLA_ERR_INVALID_ARG, "batch and n_heads must be >= 1");
+  if (d->head_dim != 128) return fail(MLA_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", d->head_dim);
+  if (d->d_c != 64 && d->d_c != 128 && d->d_c != 192 && d->d_c != 256)
+    return fail(MLA_ERR_UNSUPPORTED, "d_c must be 64, 128, 192 or 256 (got %d)", d->d_c);
+  if (d->d_r != 32) return fail(MLA_ERR_UNSUPPORTED, "d_r must be 32 (got %d)", d->d_r);
+  if (d->rope_t < 0 || d->rope_h < 0 || d->rope_w < 0 || (d->rope_t | d->rope_h | d->rope_w) & 1 ||
+      d->rope_t + d->rope_h + d->rope_w != d->d_r)
+    return fail(MLA_ERR_UNSUPPORTED, "rope widths must be even and sum to d_r (got %d/%d/%d)",
+                d->rope_t, d->rope_h, d->rope_w);
+  if (!(d->rope_theta > 0.0)) return fail(MLA_ERR_INVALID_ARG, "rope_theta must be > 0");
+  return MLA_OK;
+}
+
+int32_t check_dtype(int32_t dt, const char* name) {
+  if (dt != MLA_BF16 && dt != MLA_F32) return fail(MLA_ERR_UNSUPPORTED, "%s must be MLA_BF16 or MLA_F32 (got %d)", name, dt);
+  return MLA_OK;
+}
+
+int32_t check_ptr(const void* p, const char* name, uintptr_t align = 16) {
+  if (p == nullptr) return fail(MLA_ERR_INVALID_ARG, "%s is null", name);
+  if (!aligned(p, align)) return fail(MLA_ERR_INVALID_ARG, "%s is not %d-byte aligned", name, (int)align);
+  return MLA_OK;
+}
+
+mla::RopeSpec rope_of(const mla_dims* d) { return mla::RopeSpec{d->rope_t, d->rope_h, d->rope_w, d->rope_theta}; }
+
+// Sizes shared by the chunk-attend steps; fills the plan on success.
+int32_t check_attend_sizes(const mla_dims* d, int32_t dtype, int32_t n_q, int32_t n_k, mla::Plan* plan) {
+  int32_t st = check_dims(d);
+  if (st) return st;
+  if ((st = check_dtype(dtype, "dtype"))) return st;
+  if (n_q < 1) return fail(MLA_ERR_INVALID_ARG, "n_q must be >= 1 (got %d)", n_q);
+  if (n_k < n_q) return fail(MLA_ERR_INVALID_ARG, "n_k (%d) must be >= n_q (%d): the current chunk is part of the keys", n_k, n_q);
+  if ((int64_t)d->n_heads * n_q > (int64_t)1 << 30) return fail(MLA_ERR_UNSUPPORTED, "n_heads * n_q too large");
+  if ((int64_t)d->batch * ((int64_t)d->n_heads * n_q + 255) / 256 > (int64_t)1 << 24)
+    return fail(MLA_ERR_UNSUPPORTED, "batch * rows too large");
+  *plan = mla::make_plan(d->batch, d->n_heads, n_q, n_k, d->d_c, d->d_r, dtype == MLA_F32);
+  return MLA_OK;
+}
+
+int32_t check_workspace(const mla::Plan& p, const void* ws, int64_t bytes) {
+  if (ws == nullptr) return fail(MLA_ERR_WORKSPACE, "workspace is null");
+  if (!aligned(ws, 256)) return fail(MLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (bytes < p.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace has %lld bytes, %lld needed", (long long)bytes, (long long)p.total);
+  return MLA_OK;
+}
+
+int32_t do_absorb(const mla_dims* d, int32_t dtype, const mla::Plan& p, const void* q, const void* q_r,
+                  const int32_t* q_pos, const void* w_uk, float scale, void* ws, hipStream_t s) {
+  mla::AbsorbArgs a{};
+  a.q = q; a.q_r = q_r; a.q_pos = q_pos; a.w_uk = w_uk;
+  a.qscale = (float)((double)scale * mla::kLog2e);
+  a.qt = (char*)ws + p.off_qt;
+  a.rope = rope_of(d);
+  hipError_t e = dtype == MLA_BF16 ? mla::launch_absorb_bf16(p, a, s) : mla::launch_absorb_f32(p, a, s);
+  return finish(e, s, "mla_query_absorb");
+}
+
+int32_t do_attend(const mla_dims* d, int32_t dtype, const mla::Plan& p, const void* cache, int32_t cap,
+                  void* ws, hipStream_t s) {
+  mla::AttendArgs a{};
+  a.cache = cache;
+  a.cache_bstride = (int64_t)cap * (d->d_c + d->d_r);
+  a.workspace = ws;
+  hipError_t e = dtype == MLA_BF16 ? mla::launch_attend_bf16(p, a, s) : mla::launch_attend_f32(p, a, s);
+  return finish(e, s, "mla_latent_attend");
+}
+
+int32_t do_upproj(int32_t dtype, int32_t out_dtype, const mla::Plan& p, const void* w_uv, void* out,
+                  void* ws, hipStream_t s) {
+  mla::UpprojArgs a{};
+  a.w_uv = w_uv; a.out = out; a.out_f32 = out_dtype == MLA_F32; a.workspace = ws;
+  hipError_t e = dtype == MLA_BF16 ? mla::launch_upproj_bf16(p, a, s) : mla::launch_upproj_f32(p, a, s);
+  return finish(e, s, "mla_value_upproj");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_cache_append(const mla_dims* dims, int32_t dtype, const void* x, int32_t d_model, int32_t n_new,
+                         const void* w_dkv, const void* w_kr, const int32_t* pos_thw, void* cache,
+                         int32_t cache_capacity, int32_t write_offset, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_dtype(dtype, "dtype"))) return st;
+  if (n_new < 0) return fail(MLA_ERR_INVALID_ARG, "n_new must be >= 0");
+  if (d_model < 1) return fail(MLA_ERR_INVALID_ARG, "d_model must be >= 1");
+  if (dtype == MLA_BF16 && d_model % 32 != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "d_model must be a multiple of 32 for bf16 (got %d)", d_model);
+  if (cache_capacity < 1 || write_offset < 0 || (int64_t)write_offset + n_new > cache_capacity)
+    return fail(MLA_ERR_INVALID_ARG, "write_offset %d + n_new %d exceeds cache_capacity %d", write_offset, n_new,
+                cache_capacity);
+  if ((int64_t)dims->batch * n_new > (int64_t)1 << 30) return fail(MLA_ERR_UNSUPPORTED, "batch * n_new too large");
+  if ((st = check_ptr(x, "x"))) return st;
+  if ((st = check_ptr(w_dkv, "w_dkv"))) return st;
+  if ((st = check_ptr(w_kr, "w_kr"))) return st;
+  if ((st = check_ptr(pos_thw, "pos_thw", 4))) return st;
+  if ((st = check_ptr(cache, "cache"))) return st;
+  if (n_new == 0) return MLA_OK;
+  mla::AppendArgs a{};
+  a.batch = dims->batch; a.n_new = n_new; a.d_model = d_model; a.d_c = dims->d_c; a.d_r = dims->d_r;
+  a.cap = cache_capacity; a.off = write_offset;
+  a.x = x; a.w_dkv = w_dkv; a.w_kr = w_kr; a.pos = pos_thw; a.cache = cache;
+  a.rope = rope_of(dims);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == MLA_BF16 ? mla::launch_append_bf16(a, s) : mla::launch_append_f32(a, s);
+  return finish(e, s, "mla_cache_append");
+}
+
+int64_t mla_chunk_attend_workspace_bytes(const mla_dims* dims, int32_t dtype, int32_t n_q, int32_t n_k) {
+  mla::Plan p;
+  int32_t st = check_attend_sizes(dims, dtype, n_q, n_k, &p);
+  if (st) return st;
+  return p.total;
+}
+
+int32_t mla_query_absorb(const mla_dims* dims, int32_t dtype, const void* q, const void* q_r,
+                         const int32_t* q_pos, int32_t n_q, const void* w_uk, float softmax_scale, int32_t n_k,
+                         void* workspace, int64_t workspace_bytes, void* stream) {
+  mla::Plan p;
+  int32_t st = check_attend_sizes(dims, dtype, n_q, n_k, &p);
+  if (st) return st;
+  if ((st = check_ptr(q, "q"))) return st;
+  if ((st = check_ptr(q_r, "q_r"))) return st;
+  if ((st = check_ptr(q_pos, "q_pos", 4))) return st;
+  if ((st = check_ptr(w_uk, "w_uk"))) return st;
+  if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if ((st = check_workspace(p, workspace, workspace_bytes))) return st;
+  return do_absorb(dims, dtype, p, q, q_r, q_pos, w_uk, softmax_scale, workspace, (hipStream_t)stream);
+}
+
+int32_t mla_latent_attend(const mla_dims* dims, int32_t dtype, const void* cache, int32_t cache_capacity,
+                          int32_t n_q, int32_t n_k, void* workspace, int64_t workspace_bytes, void* stream) {
+  mla::Plan p;
+  int32_t st = check_attend_sizes(dims, dtype, n_q, n_k, &p);
+  if (st) return st;
+  if ((st = check_ptr(cache, "cache"))) return st;
+  if (n_k > cache_capacity) return fail(MLA_ERR_INVALID_ARG, "n_k (%d) exceeds cache_capacity (%d)", n_k, cache_capacity);
+  if ((st = check_workspace(p, workspace, workspace_bytes))) return st;
+  return do_attend(dims, dtype, p, cache, cache_capacity, workspace, (hipStream_t)stream);
+}
+
+int32_t mla_value_upproj(const mla_dims* dims, int32_t dtype, int32_t out_dtype, int32_t n_q, int32_t n_k,
+                         const void* w_uv, void* out, void* workspace, int64_t workspace_bytes, void* stream) {
+  mla::Plan p;
+  int32_t st = check_attend_sizes(dims, dtype, n_q, n_k, &p);
+  if (st) return st;
+  if ((st = check_dtype(out_dtype, "out_dtype"))) return st;
+  if ((st = check_ptr(w_uv, "w_uv"))) return st;
+  if ((st = check_ptr(out, "out"))) return st;
+  if ((st = check_workspace(p, workspace, workspace_bytes))) return st;
+  return do_upproj(dtype, out_dtype, p, w_uv, out, workspace, (hipStream_t)stream);
+}
+
+int32_t mla_chunk_attend(const mla_dims* dims, int32_t in_dtype, int32_t out_dtype, const void* q, const void* q_r,
+                         const int32_t* q_pos, int32_t n_q, const void* w_uk, const void* w_uv, const void* cache,
+                         int32_t cache_capacity, int32_t n_k, float softmax_scale, void* out, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  mla::Plan p;
+  int32_t st = check_attend_sizes(dims, in_dtype, n_q, n_k, &p);
+  if (st) return st;
+  if ((st = check_dtype(out_dtype, "out_dtype"))) return st;
+  if ((st = check_ptr(q, "q"))) return st;
+  if ((st = check_ptr(q_r, "q_r"))) return st;
+  if ((st = check_ptr(q_pos, "q_pos", 4))) return st;
+  if ((st = check_ptr(w_uk, "w_uk"))) return st;
+  if ((st = check_ptr(w_uv, "w_uv"))) return st;
+  if ((st = check_ptr(cache, "cache"))) return st;
+  if ((st = check_ptr(out, "out"))) return st;
+  if (n_k > cache_capacity) return fail(MLA_ERR_INVALID_ARG, "n_k (%d) exceeds cache_capacity (%d)", n_k, cache_capacity);
+  if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if ((st = check_workspace(p, workspace, workspace_bytes))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = do_absorb(dims, in_dtype, p, q, q_r, q_pos, w_uk, softmax_scale, workspace, s))) return st;
+  if ((st = do_attend(dims, in_dtype, p, cache, cache_capacity, workspace, s))) return st;
+  return do_upproj(in_dtype, out_dtype, p, w_uv, out, workspace, s);
+}
+
+const char* mla_status_string(int32_t status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+const char* mla_last_error(void) { return g_last_error; }
+
+const char* mla_version(void) { return "0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// Value up-projection with the merge of partial softmax states:
+//   L[row]   = sum_s 2^(m_s - M) L_s[row] / sum_s 2^(m_s - M) l_s[row]
+//   out[b,i,h,:] = W_UV[h] L[row]             (row = h*n_q + i of sample b)
+// The per-head W_UV is applied after attention (multi-head latent attention,
+// DeepSeek-V2, listed under "Builds on" on the VideoMLA pages), so values are
+// never materialised per head.  L stays fp32 until this product: it is split
+// as L = hi + lo with hi, lo in bf16 and both halves go through bf16 MFMA, which
+// keeps ~16 significant bits of L.
+#include "mla_common.h"
+#include "mla_kernels.h"
+
+namespace mla {
+
+// Slot holding row-block rb's segment produced by workgroup w (see Plan).
+__device__ inline int64_t seg_slot(int64_t w, int64_t rb, int64_t T, int64_t U, int64_t G) {
+  return (unit_begin(w, U, G) < rb * T) ? 2 * w + 1 : 2 * w;
+}
+
+template <int DC, bool OUT_F32>
+__global__ __launch_bounds__(256)
+void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restrict__ part_ml,
+                        int T, int64_t U, int G, int rb_per_b, int n_q, int H,
+                        const u16* __restrict__ w_uv, void* __restrict__ out) {
+  constexpr int DH = 128, KSTEPS = DC / 16;
+  const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
+  const int i = blockIdx.y * 128 + wave * 32 + (lane & 31);
+  const bool ok = i < n_q;
+  const int r = h * n_q + (ok ? i : 0);
+  const int64_t rb = (int64_t)b * rb_per_b + r / kRowsPerBlock;
+  const int rl = r % kRowsPerBlock;
+
+  // Owners of this row-block's first and last unit; merge their segments.
+  const int64_t wa = unit_owner(rb * T, U, G), wb = unit_owner(rb * T + T - 1, U, G);
+  float M = -INFINITY;
+  for (int64_t w = wa; w <= wb; ++w) {
+    const int64_t sl = seg_slot(w, rb, T, U, G);
+    M = fmaxf(M, part_ml[(sl * kRowsPerBlock + rl) * 2]);
+  }
+  float lsum = 0.f;
+  for (int64_t w = wa; w <= wb; ++w) {
+    const int64_t sl = seg_slot(w, rb, T, U, G);
+    const float* ml = part_ml + (sl * kRowsPerBlock + rl) * 2;
+    lsum += exp2f(ml[0] - M) * ml[1];
+  }
+  const float inv_l = 1.f / lsum;
+
+  f32x16 acc[DH / 32];
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db) acc[db] = f32x16{};
+  const u16* wv = w_uv + (int64_t)h * DH * DC;
+
+#pragma unroll 2
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const int c0 = ks * 16 + half * 8;
+    float lc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int64_t w = wa; w <= wb; ++w) {
+      const int64_t sl = seg_slot(w, rb, T, U, G);
+      const float wgt = exp2f(part_ml[(sl * kRowsPerBlock + rl) * 2] - M) * inv_l;
+      const f32x4* src = reinterpret_cast<const f32x4*>(part_L + (sl * kRowsPerBlock + rl) * DC + c0);
+      const f32x4 x0 = src[0], x1 = src[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { lc[e] = fmaf(wgt, x0[e], lc[e]); lc[4 + e] = fmaf(wgt, x1[e], lc[4 + e]); }
+    }
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 h2 = to_bf16x2(ok ? lc[e] : 0.f, ok ? lc[e + 1] : 0.f);
+      const bf16x2 l2 = to_bf16x2(ok ? lc[e] - (float)h2[0] : 0.f, ok ? lc[e + 1] - (float)h2[1] : 0.f);
+      hi[e] = h2[0]; hi[e + 1] = h2[1]; lo[e] = l2[0]; lo[e + 1] = l2[1];
+    }
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(wv + (int64_t)(db * 32 + (lane & 31)) * DC + c0);
+      acc[db] = mfma_32x32x16(a, hi, acc[db]);
+      acc[db] = mfma_32x32x16(a, lo, acc[db]);
+    }
+  }
+  if (!ok) return;
+  const int64_t orow = (((int64_t)b * n_q + i) * H + h) * DH;
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = db * 32 + g * 8 + half * 4;
+      if (OUT_F32) {
+        *reinterpret_cast<f32x4*>((float*)out + orow + d0) =
+            f32x4{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+      } else {
+        const uint32_t lo2 = bf16x2_bits(to_bf16x2(acc[db][4 * g], acc[db][4 * g + 1]));
+        const uint32_t hi2 = bf16x2_bits(to_bf16x2(acc[db][4 * g + 2], acc[db][4 * g + 3]));
+        *reinterpret_cast<uint2*>((u16*)out + orow + d0) = make_uint2(lo2, hi2);
+      }
+    }
+}
+
+// fp32 variant: thread per output element; L comes normalized from slot rb.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256)
+void upproj_f32_kernel(const float* __restrict__ part_L, int B, int rb_per_b, int n_q, int H, int DC,
+                       const float* __restrict__ w_uv, void* __restrict__ out) {
+  constexpr int DH = 128;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)B * n_q * H * DH;
+  if (idx >= total) return;
+  const int d = (int)(idx % DH);
+  const int64_t bih = idx / DH;
+  const int h = (int)(bih % H);
+  const int64_t bi = bih / H;
+  const int i = (int)(bi % n_q), b = (int)(bi / n_q);
+  const int r = h * n_q + i;
+  const int64_t rb = (int64_t)b * rb_per_b + r / kRowsPerBlock;
+  const float* L = part_L + (rb * kRowsPerBlock + r % kRowsPerBlock) * DC;
+  const float* wv = w_uv + ((int64_t)h * DH + d) * DC;
+  float acc = 0.f;
+  for (int c = 0; c < DC; ++c) acc = fmaf(wv[c], L[c], acc);
+  if (OUT_F32) ((float*)out)[idx] = acc;
+  else ((u16*)out)[idx] = __builtin_bit_cast(u16, (__bf16)acc);
+}
+
+hipError_t launch_upproj_bf16(const Plan& p, const UpprojArgs& a, hipStream_t s) {
+  char* ws = (char*)a.workspace;
+  const float* L = (const float*)(ws + p.off_L);
+  const float* ml = (const float*)(ws + p.off_ml);
+  const u16* wv = (const u16*)a.w_uv;
+  const dim3 grid(p.B * p.H, (p.n_q + 127) / 128), block(256);
+#define MLA_UPPROJ(DCV)                                                                                       \
+  if (a.out_f32) upproj_bf16_kernel<DCV, true><<<grid, block, 0, s>>>(L, ml, p.T, p.U, p.G, p.rb_per_b, p.n_q, p.H, wv, a.out); \
+  else upproj_bf16_kernel<DCV, false><<<grid, block, 0, s>>>(L, ml, p.T, p.U, p.G, p.rb_per_b, p.n_q, p.H, wv, a.out);
+  switch (p.d_c) {
+    case 64: MLA_UPPROJ(64) break;
+    case 128: MLA_UPPROJ(128) break;
+    case 192: MLA_UPPROJ(192) break;
+    case 256: MLA_UPPROJ(256) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MLA_UPPROJ
+  return hipGetLastError();
+}
+
+hipError_t launch_upproj_f32(const Plan& p, const UpprojArgs& a, hipStream_t s) {
+  char* ws = (char*)a.workspace;
+  const float* L = (const float*)(ws + p.off_L);
+  const int64_t total = (int64_t)p.B * p.n_q * p.H * 128;
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  if (a.out_f32)
+    upproj_f32_kernel<true><<<grid, block, 0, s>>>(L, p.B, p.rb_per_b, p.n_q, p.H, p.d_c, (const float*)a.w_uv, a.out);
+  else
+    upproj_f32_kernel<false><<<grid, block, 0, s>>>(L, p.B, p.rb_per_b, p.n_q, p.H, p.d_c, (const float*)a.w_uv, a.out);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,215 @@
+"""ctypes binding of libmla_hip.so (declared in include/mla.h).
+
+Argument marshalling only: shapes, dtypes, devices and contiguity are checked
+here, then raw device pointers and the current HIP stream are handed to the C
+ABI.  Every step of the path runs in the library's HIP kernels.  There is no
+fallback: if the library is missing or fails to load, importing this module
+raises ImportError.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_LIB_PATH = os.environ.get("MLA_HIP_LIB", os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_hip.so"))
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m latent_kv_cache_chunk_amd.build` "
+                      "(there is no CPU or PyTorch fallback)")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
+MLA_BF16, MLA_F32 = 0, 1
+
+LIB_PATH = _LIB_PATH
+EXPORTED = ("mla_cache_append", "mla_chunk_attend_workspace_bytes", "mla_chunk_attend",
+            "mla_query_absorb", "mla_latent_attend", "mla_value_upproj",
+            "mla_status_string", "mla_last_error", "mla_version")
+
+
+class MlaDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("d_c", ctypes.c_int32), ("d_r", ctypes.c_int32), ("rope_t", ctypes.c_int32),
+                ("rope_h", ctypes.c_int32), ("rope_w", ctypes.c_int32), ("rope_theta", ctypes.c_double)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_DIMS = ctypes.POINTER(MlaDims)
+
+_lib.mla_cache_append.argtypes = [_DIMS, _I32, _P, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _P]
+_lib.mla_cache_append.restype = _I32
+_lib.mla_chunk_attend_workspace_bytes.argtypes = [_DIMS, _I32, _I32, _I32]
+_lib.mla_chunk_attend_workspace_bytes.restype = _I64
+_lib.mla_chunk_attend.argtypes = [_DIMS, _I32, _I32, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32,
+                                  ctypes.c_float, _P, _P, _I64, _P]
+_lib.mla_chunk_attend.restype = _I32
+_lib.mla_query_absorb.argtypes = [_DIMS, _I32, _P, _P, _P, _I32, _P, ctypes.c_float, _I32, _P, _I64, _P]
+_lib.mla_query_absorb.restype = _I32
+_lib.mla_latent_attend.argtypes = [_DIMS, _I32, _P, _I32, _I32, _I32, _P, _I64, _P]
+_lib.mla_latent_attend.restype = _I32
+_lib.mla_value_upproj.argtypes = [_DIMS, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P]
+_lib.mla_value_upproj.restype = _I32
+_lib.mla_status_string.argtypes = [_I32]
+_lib.mla_status_string.restype = ctypes.c_char_p
+_lib.mla_last_error.argtypes = []
+_lib.mla_last_error.restype = ctypes.c_char_p
+_lib.mla_version.argtypes = []
+_lib.mla_version.restype = ctypes.c_char_p
+
+
+class MLAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = _lib.mla_last_error().decode()
+        super().__init__(f"{where}: {_lib.mla_status_string(code).decode()} ({code}): {msg}")
+
+
+@dataclass(frozen=True)
+class Dims:
+    batch: int
+    n_heads: int = 12
+    head_dim: int = 128
+    d_c: int = 192
+    d_r: int = 32
+    rope: tuple = (8, 12, 12)
+    rope_theta: float = 1e4
+
+    def c(self) -> MlaDims:
+        return MlaDims(self.batch, self.n_heads, self.head_dim, self.d_c, self.d_r,
+                       self.rope[0], self.rope[1], self.rope[2], float(self.rope_theta))
+
+
+def version() -> str:
+    return _lib.mla_version().decode()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return MLA_BF16
+    if t == torch.float32:
+        return MLA_F32
+    raise TypeError(f"unsupported dtype {t} (bfloat16 or float32)")
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _raise(code: int, where: str):
+    if code != MLA_OK:
+        raise MLAError(code, where)
+
+
+def cache_append(dims: Dims, x, w_dkv, w_kr, pos, cache, offset: int, stream=None) -> None:
+    """Write [W_DKV x || RoPE3D(pos) W_KR x] rows of the new tokens into cache[:, offset:offset+n]."""
+    B, n_new, D = x.shape
+    dt = x.dtype
+    _check(x, "x", (dims.batch, n_new, D), dt)
+    _check(w_dkv, "w_dkv", (dims.d_c, D), dt)
+    _check(w_kr, "w_kr", (dims.d_r, D), dt)
+    _check(pos, "pos", (n_new, 3), torch.int32)
+    cap = cache.shape[1]
+    _check(cache, "cache", (dims.batch, cap, dims.d_c + dims.d_r), dt)
+    d = dims.c()
+    code = _lib.mla_cache_append(ctypes.byref(d), _dtype_code(dt), x.data_ptr(), D, n_new, w_dkv.data_ptr(),
+                                 w_kr.data_ptr(), pos.data_ptr(), cache.data_ptr(), cap, int(offset),
+                                 _stream(stream))
+    _raise(code, "mla_cache_append")
+
+
+def workspace_bytes(dims: Dims, dtype: torch.dtype, n_q: int, n_k: int) -> int:
+    d = dims.c()
+    n = _lib.mla_chunk_attend_workspace_bytes(ctypes.byref(d), _dtype_code(dtype), int(n_q), int(n_k))
+    if n < 0:
+        _raise(int(n), "mla_chunk_attend_workspace_bytes")
+    return int(n)
+
+
+def alloc_workspace(dims: Dims, dtype: torch.dtype, n_q: int, n_k: int, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(dims, dtype, n_q, n_k)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _attend_checks(dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k):
+    B, n_q, H, dh = q.shape
+    dt = q.dtype
+    _check(q, "q", (dims.batch, n_q, dims.n_heads, dims.head_dim), dt)
+    _check(q_r, "q_r", (dims.batch, n_q, dims.n_heads, dims.d_r), dt)
+    _check(q_pos, "q_pos", (n_q, 3), torch.int32)
+    if w_uk is not None:
+        _check(w_uk, "w_uk", (dims.n_heads, dims.head_dim, dims.d_c), dt)
+    if w_uv is not None:
+        _check(w_uv, "w_uv", (dims.n_heads, dims.head_dim, dims.d_c), dt)
+    if cache is not None:
+        _check(cache, "cache", (dims.batch, cache.shape[1], dims.d_c + dims.d_r), dt)
+    return n_q, dt
+
+
+def chunk_attend(dims: Dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k: int, scale: float,
+                 out=None, out_dtype=None, workspace=None, stream=None) -> torch.Tensor:
+    """out[b,i,h] = sum_j softmax_j(scale*(q.k_h + RoPE(p_i)q_r.k_R)) W_UV[h] c_j over keys j < n_k."""
+    n_q, dt = _attend_checks(dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k)
+    odt = dt if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((dims.batch, n_q, dims.n_heads, dims.head_dim), dtype=odt, device=q.device)
+    _check(out, "out", (dims.batch, n_q, dims.n_heads, dims.head_dim), odt)
+    if workspace is None:
+        workspace = alloc_workspace(dims, dt, n_q, n_k, q.device)
+    d = dims.c()
+    code = _lib.mla_chunk_attend(ctypes.byref(d), _dtype_code(dt), _dtype_code(odt), q.data_ptr(), q_r.data_ptr(),
+                                 q_pos.data_ptr(), n_q, w_uk.data_ptr(), w_uv.data_ptr(), cache.data_ptr(),
+                                 cache.shape[1], int(n_k), float(scale), out.data_ptr(), workspace.data_ptr(),
+                                 workspace.numel(), _stream(stream))
+    _raise(code, "mla_chunk_attend")
+    return out
+
+
+def query_absorb(dims: Dims, q, q_r, q_pos, w_uk, scale: float, n_k: int, workspace, stream=None) -> None:
+    n_q, dt = _attend_checks(dims, q, q_r, q_pos, w_uk, None, None, n_k)
+    d = dims.c()
+    code = _lib.mla_query_absorb(ctypes.byref(d), _dtype_code(dt), q.data_ptr(), q_r.data_ptr(), q_pos.data_ptr(),
+                                 n_q, w_uk.data_ptr(), float(scale), int(n_k), workspace.data_ptr(),
+                                 workspace.numel(), _stream(stream))
+    _raise(code, "mla_query_absorb")
+
+
+def latent_attend(dims: Dims, cache, n_q: int, n_k: int, workspace, stream=None) -> None:
+    _check(cache, "cache", (dims.batch, cache.shape[1], dims.d_c + dims.d_r), cache.dtype)
+    d = dims.c()
+    code = _lib.mla_latent_attend(ctypes.byref(d), _dtype_code(cache.dtype), cache.data_ptr(), cache.shape[1],
+                                  int(n_q), int(n_k), workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _raise(code, "mla_latent_attend")
+
+
+def value_upproj(dims: Dims, w_uv, out, n_q: int, n_k: int, workspace, stream=None) -> None:
+    _check(w_uv, "w_uv", (dims.n_heads, dims.head_dim, dims.d_c), w_uv.dtype)
+    _check(out, "out", (dims.batch, n_q, dims.n_heads, dims.head_dim), out.dtype)
+    d = dims.c()
+    code = _lib.mla_value_upproj(ctypes.byref(d), _dtype_code(w_uv.dtype), _dtype_code(out.dtype), int(n_q),
+                                 int(n_k), w_uv.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                                 workspace.numel(), _stream(stream))
+    _raise(code, "mla_value_upproj")
+
+
+def raw():
+    """The loaded ctypes library (for tests of the C ABI itself)."""
+    return _lib

@@ -11,3 +11,13 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running case")
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    # Name the case on the real stderr (not captured) before a GPU test runs,
+    # so a run that dies inside a kernel still says which case it was.
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

@@ -1,0 +1,53 @@
+"""Helpers shared by the GPU parity tests (comparison metrics only)."""
+
+import numpy as np
+import pytest
+import torch
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs an MI355X")
+    from latent_kv_cache_chunk_amd import mla  # noqa: F401  (fails loudly if the library is missing)
+    return mla
+
+
+def np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def errors(got: np.ndarray, want: np.ndarray) -> dict:
+    d = np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))
+    rms = float(np.sqrt(np.mean(np.square(want))))
+    return dict(max_abs=float(d.max()), mean_abs=float(d.mean()), rms_ref=rms,
+                max_norm=float(d.max() / rms), mean_norm=float(d.mean() / rms))
+
+
+# Gates on chunk attention output (see the test docstrings for the reasoning):
+#   G1 raw absolute error of the bf16 output on unit-scale values
+G1_MAX, G1_MEAN = 2e-2, 2e-3
+#   G2 error of the fp32-output path divided by the RMS of the reference output
+G2_MAX, G2_MEAN = 2e-2, 2e-3
+#   fp32 inputs, fp32 output, divided by the RMS of the reference output
+F32_MAX, F32_MEAN = 1e-4, 1e-5
+
+
+def assert_g1(got, want, label=""):
+    e = errors(got, want)
+    assert np.all(np.isfinite(got)), label
+    assert e["max_abs"] <= G1_MAX and e["mean_abs"] <= G1_MEAN, (label, e)
+    return e
+
+
+def assert_g2(got, want, label=""):
+    e = errors(got, want)
+    assert np.all(np.isfinite(got)), label
+    assert e["max_norm"] <= G2_MAX and e["mean_norm"] <= G2_MEAN, (label, e)
+    return e
+
+
+def assert_f32(got, want, label=""):
+    e = errors(got, want)
+    assert np.all(np.isfinite(got)), label
+    assert e["max_norm"] <= F32_MAX and e["mean_norm"] <= F32_MEAN, (label, e)
+    return e

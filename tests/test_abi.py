@@ -1,0 +1,143 @@
+"""Host-side tests of the C ABI: symbols, status codes, validation, planning.
+
+None of these enqueue GPU work: every call here either is pure host logic or
+fails validation before anything is launched, so they run without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+mla = pytest.importorskip("latent_kv_cache_chunk_amd.mla",
+                          reason="libmla_hip.so not built (python -m latent_kv_cache_chunk_amd.build)")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = mla.raw()
+    names = _declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/mla.h but not exported"
+    assert set(names) == set(mla.EXPORTED)
+
+
+def test_exported_symbols_are_c_linkage():
+    # nm on our own build output: the ABI symbols must be unmangled.
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in _declared_functions():
+        assert n in syms
+
+
+def test_status_strings_and_version():
+    lib = mla.raw()
+    assert lib.mla_status_string(0) == b"MLA_OK"
+    assert lib.mla_status_string(-1) == b"MLA_ERR_INVALID_ARG"
+    assert lib.mla_status_string(-2) == b"MLA_ERR_UNSUPPORTED"
+    assert lib.mla_status_string(-3) == b"MLA_ERR_WORKSPACE"
+    assert lib.mla_status_string(-4) == b"MLA_ERR_HIP"
+    assert lib.mla_status_string(17) == b"MLA_ERR_UNKNOWN"
+    assert b"gfx950" in lib.mla_version()
+
+
+def _dims(**kw):
+    base = dict(batch=1, n_heads=12, head_dim=128, d_c=192, d_r=32, rope=(8, 12, 12), rope_theta=1e4)
+    base.update(kw)
+    return mla.Dims(**base).c()
+
+
+def _ws(d, dt=0, n_q=48, n_k=192):
+    return mla.raw().mla_chunk_attend_workspace_bytes(ctypes.byref(d), dt, n_q, n_k)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), -2), (dict(d_c=100), -2), (dict(d_c=320), -2), (dict(d_r=64, rope=(16, 24, 24)), -2),
+    (dict(rope=(8, 12, 10)), -2), (dict(rope=(7, 13, 12)), -2), (dict(batch=0), -1), (dict(n_heads=0), -1),
+    (dict(rope_theta=0.0), -1),
+])
+def test_invalid_dims_are_rejected(kw, code):
+    assert _ws(_dims(**kw)) == code
+
+
+def test_invalid_sizes_and_dtypes():
+    d = _dims()
+    assert _ws(d, n_q=0, n_k=10) == -1
+    assert _ws(d, n_q=50, n_k=49) == -1          # the chunk's own keys are part of n_k
+    assert _ws(d, dt=7) == -2
+    assert mla.raw().mla_chunk_attend_workspace_bytes(None, 0, 48, 192) == -1
+
+
+def test_workspace_plan_sizes():
+    # 480P: 56160 rows -> 220 row-blocks of 256; 512 key tiles; stream-K over 256 workgroups.
+    d = _dims()
+    n480 = _ws(d, 0, 4680, 32760)
+    rows_pad = 220 * 256
+    qt = rows_pad * 224 * 2
+    slots = 2 * 256
+    assert n480 >= qt + slots * 256 * (192 + 2) * 4
+    assert n480 < qt + slots * 256 * (192 + 2) * 4 + 4096
+    # fp32 variant: one slot per row-block
+    n32 = _ws(d, 1, 48, 192)
+    assert n32 >= 3 * 256 * 224 * 4 + 3 * 256 * 194 * 4
+
+
+def test_calls_fail_validation_without_launching():
+    lib = mla.raw()
+    d = _dims()
+    fake = ctypes.c_void_p(0x10000)        # aligned, never dereferenced: validation fails first
+    # null query pointer
+    rc = lib.mla_chunk_attend(ctypes.byref(d), 0, 0, None, fake, fake, 48, fake, fake, fake, 192, 192,
+                              ctypes.c_float(0.08), fake, fake, 1 << 40, None)
+    assert rc == -1 and b"q is null" in lib.mla_last_error()
+    # misaligned cache
+    rc = lib.mla_chunk_attend(ctypes.byref(d), 0, 0, fake, fake, fake, 48, fake, fake, ctypes.c_void_p(0x10002),
+                              192, 192, ctypes.c_float(0.08), fake, fake, 1 << 40, None)
+    assert rc == -1 and b"aligned" in lib.mla_last_error()
+    # n_k beyond capacity
+    rc = lib.mla_chunk_attend(ctypes.byref(d), 0, 0, fake, fake, fake, 48, fake, fake, fake, 100, 192,
+                              ctypes.c_float(0.08), fake, fake, 1 << 40, None)
+    assert rc == -1 and b"capacity" in lib.mla_last_error()
+    # workspace too small
+    rc = lib.mla_chunk_attend(ctypes.byref(d), 0, 0, fake, fake, fake, 48, fake, fake, fake, 192, 192,
+                              ctypes.c_float(0.08), fake, fake, 1024, None)
+    assert rc == -3
+    # bad scale
+    rc = lib.mla_chunk_attend(ctypes.byref(d), 0, 0, fake, fake, fake, 48, fake, fake, fake, 192, 192,
+                              ctypes.c_float(-1.0), fake, fake, 1 << 40, None)
+    assert rc == -1
+    # append: offset + n_new beyond capacity, bad d_model
+    rc = lib.mla_cache_append(ctypes.byref(d), 0, fake, 1536, 48, fake, fake, fake, fake, 100, 60, None)
+    assert rc == -1
+    rc = lib.mla_cache_append(ctypes.byref(d), 0, fake, 1530, 48, fake, fake, fake, fake, 100, 0, None)
+    assert rc == -2
+    rc = lib.mla_cache_append(ctypes.byref(d), 0, fake, 1536, -1, fake, fake, fake, fake, 100, 0, None)
+    assert rc == -1
+    # append of zero tokens is a valid no-op (nothing enqueued)
+    rc = lib.mla_cache_append(ctypes.byref(d), 0, fake, 1536, 0, fake, fake, fake, fake, 100, 100, None)
+    assert rc == 0
+    # steps share the size checks
+    assert lib.mla_latent_attend(ctypes.byref(d), 0, fake, 100, 48, 192, fake, 1 << 40, None) == -1
+    assert lib.mla_value_upproj(ctypes.byref(d), 0, 5, 48, 192, fake, fake, fake, 1 << 40, None) == -2
+    assert lib.mla_query_absorb(ctypes.byref(d), 0, fake, fake, fake, 48, fake, ctypes.c_float(0.1), 192,
+                                None, 1 << 40, None) == -3
+
+
+def test_binding_checks_tensors_on_host():
+    d = mla.Dims(batch=1)
+    with pytest.raises(ValueError):
+        mla.cache_append(d, torch.zeros(1, 4, 64, dtype=torch.bfloat16), torch.zeros(192, 64, dtype=torch.bfloat16),
+                         torch.zeros(32, 64, dtype=torch.bfloat16), torch.zeros(4, 3, dtype=torch.int32),
+                         torch.zeros(1, 8, 224, dtype=torch.bfloat16), 0)

@@ -1,0 +1,248 @@
+"""GPU parity of chunk attention (absorb -> fused attend -> up-projection)
+against the fp64 non-absorbed oracle, called through the C ABI.
+
+Gates (unit-scale outputs: the values W_UV c have unit variance under the
+input recipe):
+  G1  bf16 output:  raw max |err| <= 2e-2, raw mean |err| <= 2e-3.
+  G2  bf16 inputs, fp32 output: errors divided by RMS(oracle) satisfy the
+      same 2e-2 / 2e-3 (the output of attention is a weighted mean, so its
+      RMS is well below 1 and raw errors alone would be a weak test).
+  F32 fp32 inputs and output: RMS-normalised max <= 1e-4, mean <= 1e-5.
+Small shapes are compared element by element; the full workload shapes are
+compared on sampled rows that the oracle computes one by one.
+"""
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from latent_kv_cache_chunk_amd import synth
+from tests.gpu_util import assert_f32, assert_g1, assert_g2, errors, need_gpu, np64
+
+pytestmark = pytest.mark.gpu
+
+
+def _dims(mla, wl):
+    return mla.Dims(batch=wl.batch, n_heads=wl.n_heads, head_dim=wl.head_dim, d_c=wl.d_c, d_r=wl.d_r,
+                    rope=wl.rope_split, rope_theta=wl.theta)
+
+
+def _dev(inp):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def _gpu(mla, wl, inp, out_dtype=None, workspace=None):
+    d = _dev(inp)
+    out = mla.chunk_attend(_dims(mla, wl), d["q"], d["q_r"], d["q_pos"], d["w_uk"], d["w_uv"], d["cache"],
+                           inp["n_k"], inp["scale"], out_dtype=out_dtype, workspace=workspace)
+    torch.cuda.synchronize()
+    return np64(out)
+
+
+def _oracle(wl, inp):
+    return oracle.chunk_attend(np64(inp["q"]), np64(inp["q_r"]), inp["q_pos"].numpy(), np64(inp["w_uk"]),
+                               np64(inp["w_uv"]), np64(inp["cache"]), inp["n_k"], inp["scale"],
+                               split=wl.rope_split, theta=wl.theta)
+
+
+def _oracle_rows(wl, inp, rows):
+    return oracle.chunk_attend_rows(rows, np64(inp["q"]), np64(inp["q_r"]), inp["q_pos"].numpy(),
+                                    np64(inp["w_uk"]), np64(inp["w_uv"]), np64(inp["cache"]), inp["n_k"],
+                                    inp["scale"], split=wl.rope_split, theta=wl.theta)
+
+
+def _sample_rows(wl, n, seed=0, heads=None):
+    rng = np.random.default_rng(seed)
+    hs = np.arange(wl.n_heads) if heads is None else np.asarray(heads)
+    b = rng.integers(0, wl.batch, n)
+    i = rng.integers(0, wl.n_q, n)
+    h = rng.choice(hs, n)
+    rows = np.stack([b, i, h], 1)
+    edge = np.array([[0, 0, hs[0]], [wl.batch - 1, wl.n_q - 1, hs[-1]], [0, wl.n_q - 1, hs[0]]])
+    return np.concatenate([edge, rows], 0)
+
+
+# ----------------------------------------------------------------------- tiny
+def test_tiny_bf16_g1():
+    mla = need_gpu()
+    wl = synth.TINY
+    inp = synth.attend_inputs(wl, seed=0)
+    assert_g1(_gpu(mla, wl, inp), _oracle(wl, inp), "tiny bf16")
+
+
+def test_tiny_bf16_fp32_out_g2():
+    mla = need_gpu()
+    wl = synth.TINY
+    inp = synth.attend_inputs(wl, seed=0)
+    assert_g2(_gpu(mla, wl, inp, out_dtype=torch.float32), _oracle(wl, inp), "tiny bf16->f32")
+
+
+def test_tiny_fp32():
+    mla = need_gpu()
+    wl = synth.TINY
+    inp = synth.attend_inputs(wl, seed=0, dtype=torch.float32)
+    assert_f32(_gpu(mla, wl, inp), _oracle(wl, inp), "tiny fp32")
+
+
+# -------------------------------------------------- ragged shapes, every d_c
+@pytest.mark.parametrize("d_c", [64, 128, 192, 256])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_ragged_shapes(d_c, dtype):
+    mla = need_gpu()
+    # 37 queries x 3 heads (ragged row block), 150 keys (ragged key tile), 2 samples
+    wl = replace(synth.TINY, batch=2, n_heads=3, d_c=d_c, grid_hw=(37, 1), query_frames=(9,),
+                 cache_frames=(0, 1, 2))                  # 3*37 cached + 37 current = 148 keys
+    inp = synth.attend_inputs(wl, seed=5, dtype=dtype, capacity=wl.n_k + 9)
+    got = _gpu(mla, wl, inp, out_dtype=torch.float32)
+    want = _oracle(wl, inp)
+    if dtype == torch.float32:
+        assert_f32(got, want, f"ragged f32 dc{d_c}")
+    else:
+        assert_g2(got, want, f"ragged bf16 dc{d_c}")
+
+
+def test_stream_k_partial_segments():
+    """15 row-blocks over 256 workgroups: every row-block is split across many segments."""
+    mla = need_gpu()
+    wl = replace(synth.TINY, grid_hw=(30, 10), query_frames=(6,), cache_frames=tuple(range(6)))  # 300 q, 2100 k
+    inp = synth.attend_inputs(wl, seed=6)
+    want = _oracle(wl, inp)
+    assert_g1(_gpu(mla, wl, inp), want, "stream-k bf16")
+    assert_g2(_gpu(mla, wl, inp, out_dtype=torch.float32), want, "stream-k bf16->f32")
+
+
+def test_unsplit_partition():
+    """235 row-blocks: one workgroup per row-block, no key partition."""
+    mla = need_gpu()
+    wl = replace(synth.TINY, grid_hw=(50, 100), query_frames=(1,), cache_frames=())     # 5000 q, 5000 k
+    inp = synth.attend_inputs(wl, seed=7)
+    rows = _sample_rows(wl, 200, seed=1)
+    got = _gpu(mla, wl, inp, out_dtype=torch.float32)
+    want = _oracle_rows(wl, inp, rows)
+    assert_g2(got[rows[:, 0], rows[:, 1], rows[:, 2]], want, "unsplit")
+
+
+def test_peaky_logits():
+    """q and q_r scaled x8: logits with std 8 exercise the running-max rescale.
+
+    The absorbed query is rounded once to bf16 (relative error 2^-9), so the
+    logit error grows in proportion to the logit magnitude; the gate is the
+    unit-scale G1 gate scaled by that factor (8), halved for margin: a
+    rescale bug gives errors of order 1.
+    """
+    mla = need_gpu()
+    wl = replace(synth.TINY, grid_hw=(12, 10), query_frames=(4,), cache_frames=tuple(range(4)))
+    inp = synth.attend_inputs(wl, seed=8)
+    inp["q"] = (inp["q"].float() * 8).to(torch.bfloat16)
+    inp["q_r"] = (inp["q_r"].float() * 8).to(torch.bfloat16)
+    want = _oracle(wl, inp)
+    for out_dtype in (None, torch.float32):
+        e = errors(_gpu(mla, wl, inp, out_dtype=out_dtype), want)
+        assert e["max_abs"] <= 4 * 2e-2 and e["mean_abs"] <= 4 * 2e-3, e
+
+
+def test_max_key_at_tile_edges():
+    """One key far above the rest, placed first, last, and at a tile boundary."""
+    mla = need_gpu()
+    wl = replace(synth.TINY, n_heads=2)
+    for j in (0, wl.n_k - 1, 64, 63):
+        inp = synth.attend_inputs(wl, seed=9)
+        c = inp["cache"].float()
+        q0 = inp["q"][0, 0, 0].float()
+        # make key j align with query (0,0,0) through W_UK of head 0
+        k_dir = inp["w_uk"][0].float().T @ q0                     # latent direction seen by that query
+        c[0, j, :wl.d_c] = 6.0 * k_dir / k_dir.norm()
+        inp["cache"] = c.to(torch.bfloat16)
+        want = _oracle(wl, inp)
+        assert_g1(_gpu(mla, wl, inp), want, f"max key at {j}")
+
+
+# ---------------------------------------------------- full workload shapes
+@pytest.mark.parametrize("name", ["wan480p", "wan720p_long"])
+def test_full_shape_sampled_rows(name):
+    mla = need_gpu()
+    wl = synth.WORKLOADS[name]
+    inp = synth.attend_inputs(wl, seed=0)
+    rows = _sample_rows(wl, 96, seed=2, heads=[0, 5, 11])
+    got = _gpu(mla, wl, inp)
+    want = _oracle_rows(wl, inp, rows)
+    assert_g1(got[rows[:, 0], rows[:, 1], rows[:, 2]], want, name)
+    got32 = _gpu(mla, wl, inp, out_dtype=torch.float32)
+    assert_g2(got32[rows[:, 0], rows[:, 1], rows[:, 2]], want, name + " f32 out")
+    assert np.all(np.isfinite(got))
+
+
+def test_batched_480p_sampled_rows():
+    mla = need_gpu()
+    wl = synth.WAN480P_B8
+    inp = synth.attend_inputs(wl, seed=0)
+    rows = _sample_rows(wl, 64, seed=3, heads=[2, 9])
+    got = _gpu(mla, wl, inp, out_dtype=torch.float32)
+    want = _oracle_rows(wl, inp, rows)
+    assert_g2(got[rows[:, 0], rows[:, 1], rows[:, 2]], want, "480p b8")
+
+
+@pytest.mark.parametrize("d_c", [64, 128, 256])
+def test_dc_sweep_480p_sampled_rows(d_c):
+    mla = need_gpu()
+    wl = synth.WAN480P.with_dc(d_c)
+    inp = synth.attend_inputs(wl, seed=0)
+    rows = _sample_rows(wl, 48, seed=4, heads=[1, 7])
+    got = _gpu(mla, wl, inp, out_dtype=torch.float32)
+    want = _oracle_rows(wl, inp, rows)
+    assert_g2(got[rows[:, 0], rows[:, 1], rows[:, 2]], want, f"480p dc{d_c}")
+
+
+# ------------------------------------------------ composition and hygiene
+def test_steps_compose_to_chunk_attend():
+    mla = need_gpu()
+    wl = replace(synth.TINY, grid_hw=(30, 10), query_frames=(6,), cache_frames=tuple(range(6)))
+    inp = _dev(synth.attend_inputs(wl, seed=10))
+    d = _dims(mla, wl)
+    ws = mla.alloc_workspace(d, torch.bfloat16, wl.n_q, wl.n_k)
+    full = mla.chunk_attend(d, inp["q"], inp["q_r"], inp["q_pos"], inp["w_uk"], inp["w_uv"], inp["cache"],
+                            wl.n_k, wl.scale, workspace=ws)
+    out = torch.empty_like(full)
+    mla.query_absorb(d, inp["q"], inp["q_r"], inp["q_pos"], inp["w_uk"], wl.scale, wl.n_k, ws)
+    mla.latent_attend(d, inp["cache"], wl.n_q, wl.n_k, ws)
+    mla.value_upproj(d, inp["w_uv"], out, wl.n_q, wl.n_k, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int16), out.view(torch.int16))
+
+
+def test_deterministic_and_poisoned_workspace():
+    mla = need_gpu()
+    wl = replace(synth.TINY, grid_hw=(30, 10), query_frames=(6,), cache_frames=tuple(range(6)))
+    inp = synth.attend_inputs(wl, seed=11)
+    d = _dims(mla, wl)
+    ws = mla.alloc_workspace(d, torch.bfloat16, wl.n_q, wl.n_k)
+    ws.fill_(0xFF)                          # NaN in every fp32 / bf16 slot
+    a = _gpu(mla, wl, inp, workspace=ws)
+    ws.fill_(0x7F)
+    b = _gpu(mla, wl, inp, workspace=ws)
+    assert np.all(np.isfinite(a))
+    assert np.array_equal(a, b)
+
+
+def test_append_then_attend_chunk_step():
+    """One chunk step: append the current chunk's rows, then attend over all keys."""
+    mla = need_gpu()
+    wl = replace(synth.TINY, grid_hw=(8, 12), query_frames=(6, 7), cache_frames=tuple(range(6)))
+    att = synth.attend_inputs(wl, seed=12, capacity=wl.n_k + 32)
+    app = synth.append_inputs(wl, seed=12)
+    d = _dims(mla, wl)
+    cache = att["cache"].cuda()
+    mla.cache_append(d, app["x"].cuda(), app["w_dkv"].cuda(), app["w_kr"].cuda(), app["pos"].cuda(), cache,
+                     wl.n_cached)
+    att_dev = _dev(att)
+    out = mla.chunk_attend(d, att_dev["q"], att_dev["q_r"], att_dev["q_pos"], att_dev["w_uk"], att_dev["w_uv"],
+                           cache, wl.n_k, wl.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_cache = oracle.cache_append(np64(att["cache"]), np64(app["x"]), np64(app["w_dkv"]), np64(app["w_kr"]),
+                                    app["pos"].numpy(), wl.n_cached)
+    inp = dict(att)
+    inp["cache"] = torch.from_numpy(ref_cache).to(torch.bfloat16)
+    assert_g2(np64(out), _oracle(wl, inp), "append+attend")
