@@ -1,0 +1,195 @@
+"""Benchmark of one chunk step of latent-KV (MLA) chunk attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload wan480p] [--no-cpu-baseline]
+
+A step is the whole hot path over one synthetic batch: cache append of the
+current chunk (latent down-projection + rotated positional key), query
+absorption, the fused latent attention over every cached chunk plus the
+current one, and the merge + W_UV up-projection.  Inputs are resident in HBM
+before the timed region.  Timing uses HIP events on the stream the library
+launches on (torch's current stream); per-kernel durations are events around
+each call inside the timed steps.
+
+Prints one JSON line.  `value` is algorithmic TFLOP/s of the step (absorbed
+count: B*Nq*H*[Nk*(4 d_c + 2 d_r) + 4 d_h d_c] plus the append's
+2*B*Nq*D*(d_c + d_r)).  `roofline` is for the dominant kernel (the fused
+attention: 2(d_c+d_r) + 2 d_c flop per (row, key)); `cpu_baseline` is the
+fp64 oracle timed on this host on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA chunk-attention TFLOP/s + ms/chunk (480P, d_c=192); % bf16 MFMA peak"
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+HBM_PEAK_GBS = 8000.0
+ATTEND_SOURCES = ("latent_kv_cache_chunk_amd/csrc/attend.hip", "latent_kv_cache_chunk_amd/csrc/mla_common.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in ATTEND_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per attend launch from committed rocprofv3 counters, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", f"attend_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, inputs, n_heads: int) -> dict:
+    """Time the fp64 oracle (as it stands) on a bounded sample of the workload:
+    every query row of the first `n_heads` heads of sample 0, against all keys."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    hh, ii = np.meshgrid(np.arange(min(n_heads, wl.n_heads)), np.arange(wl.n_q), indexing="ij")
+    rows = np.stack([np.zeros(hh.size, np.int64), ii.ravel(), hh.ravel()], 1)   # batch 0
+    args = [inputs[k].cpu().double().numpy() for k in ("q", "q_r")]
+    q_pos = inputs["q_pos"].cpu().numpy()
+    w_uk = inputs["w_uk"].cpu().double().numpy()
+    w_uv = inputs["w_uv"].cpu().double().numpy()
+    cache = inputs["cache"][:, :wl.n_k].cpu().double().numpy()
+    t0 = time.perf_counter()
+    oracle.chunk_attend_rows(rows, args[0], args[1], q_pos, w_uk, w_uv, cache, wl.n_k, wl.scale,
+                             split=wl.rope_split, theta=wl.theta)
+    dt = time.perf_counter() - t0
+    flops = len(rows) * (wl.n_k * (4 * wl.d_c + 2 * wl.d_r) + 4 * wl.head_dim * wl.d_c)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(rows)} rows (all {wl.n_q} queries of heads 0..{min(n_heads, wl.n_heads) - 1}, "
+                      f"batch 0) against all {wl.n_k} keys, fp64 "
+                      f"non-absorbed numpy oracle incl. per-head K/V reconstruction; {dt:.1f} s wall; "
+                      f"rate = absorbed algorithmic flops of the sample / wall time"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="wan480p")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=12, help="heads whose rows form the oracle sample")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "only one GPU is measured: run with --gpus 1 "
+                                   "(the path would shard by batch or query rows over a replicated latent cache)", "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+    from latent_kv_cache_chunk_amd import mla, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    dims = mla.Dims(batch=wl.batch, n_heads=wl.n_heads, head_dim=wl.head_dim, d_c=wl.d_c, d_r=wl.d_r,
+                    rope=wl.rope_split, rope_theta=wl.theta)
+    att = synth.attend_inputs(wl, seed=args.seed)
+    app = synth.append_inputs(wl, seed=args.seed)
+    t = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in att.items()}
+    a = {k: v.to(dev) for k, v in app.items()}
+    cache = t["cache"]
+    ws = mla.alloc_workspace(dims, torch.bfloat16, wl.n_q, wl.n_k, dev)
+    out = torch.empty((wl.batch, wl.n_q, wl.n_heads, wl.head_dim), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        mla.cache_append(dims, a["x"], a["w_dkv"], a["w_kr"], a["pos"], cache, wl.n_cached)
+        if ev is not None:
+            ev[1].record()
+        mla.query_absorb(dims, t["q"], t["q_r"], t["q_pos"], t["w_uk"], wl.scale, wl.n_k, ws)
+        if ev is not None:
+            ev[2].record()
+        mla.latent_attend(dims, cache, wl.n_q, wl.n_k, ws)
+        if ev is not None:
+            ev[3].record()
+        mla.value_upproj(dims, t["w_uv"], out, wl.n_q, wl.n_k, ws)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])   # [steps, 4]
+    append_ms, absorb_ms, attend_ms, upproj_ms = (float(np.mean(per[:, j])) for j in range(4))
+    attend_ms_median = float(np.median(per[:, 2]))
+
+    step_flops = wl.attend_flops() + wl.append_flops()
+    core_flops = wl.attend_core_flops()
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    attend_tflops = core_flops / (attend_ms * 1e-3) / 1e12
+    traffic = load_traffic(wl.name)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian inputs of the workload's shape)",
+        "config": {"workload": wl.name, "batch": wl.batch, "n_q": wl.n_q, "n_k": wl.n_k,
+                   "heads": wl.n_heads, "head_dim": wl.head_dim, "d_c": wl.d_c, "d_r": wl.d_r,
+                   "rope_split": list(wl.rope_split), "d_model": wl.d_model},
+        "frac_bf16_peak": round(value / BF16_PEAK_TFLOPS, 4),
+        "breakdown_ms": {"append": round(append_ms, 4), "absorb": round(absorb_ms, 4),
+                         "attend": round(attend_ms, 4), "attend_median": round(attend_ms_median, 4),
+                         "upproj_merge": round(upproj_ms, 4)},
+        "mha_equiv_tflops": round(wl.mha_equiv_flops() / (ms_step * 1e-3) / 1e12, 2),
+        "roofline": {"kernel": "attend_bf16_kernel", "bound": "mfma",
+                     "achieved": round(attend_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attend_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "flop_per_launch": core_flops,
+                     "per_unit": f"{4 * wl.d_c + 2 * wl.d_r} flop per (row, key); "
+                                 f"{wl.batch * wl.n_q * wl.n_heads} rows x {wl.n_k} keys per launch"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, att, args.cpu_heads)
+    print(json.dumps(res))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
