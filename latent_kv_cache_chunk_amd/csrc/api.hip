@@ -41,6 +41,16 @@ int32_t finish(hipError_t launched, hipStream_t s, const char* what) {
   return MLA_OK;
 }
 
+// Headroom (log2 units) the single-pass attention allows above a segment's
+// first-block max before it redoes the segment in two exact passes.  32 by
+// default; MLA_ATTEND_HEADROOM (read at every call) overrides it, so tests can
+// set it small and exercise the two-pass path on ordinary inputs.
+float attend_headroom() {
+  const char* v = getenv("MLA_ATTEND_HEADROOM");
+  const float x = v ? (float)atof(v) : 32.0f;
+  return (x >= 0.f && x <= 64.f) ? x : 32.0f;
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int32_t check_dims(const mla_dims* d) {
@@ -110,6 +120,7 @@ int32_t do_attend(const mla_dims* d, int32_t dtype, const mla::Plan& p, const vo
   a.cache = cache;
   a.cache_bstride = (int64_t)cap * (d->d_c + d->d_r);
   a.workspace = ws;
+  a.headroom = attend_headroom();
   hipError_t e = dtype == MLA_BF16 ? mla::launch_attend_bf16(p, a, s) : mla::launch_attend_f32(p, a, s);
   return finish(e, s, "mla_latent_attend");
 }

@@ -29,6 +29,7 @@ struct AttendArgs {
   const void* cache;
   int64_t cache_bstride;  // elements between samples (capacity * width)
   void* workspace;
+  float headroom;         // log2 headroom of the single-pass softmax (see attend.hip)
 };
 
 struct UpprojArgs {

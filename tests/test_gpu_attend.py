@@ -246,3 +246,16 @@ def test_append_then_attend_chunk_step():
     inp = dict(att)
     inp["cache"] = torch.from_numpy(ref_cache).to(torch.bfloat16)
     assert_g2(np64(out), _oracle(wl, inp), "append+attend")
+
+
+@pytest.mark.parametrize("headroom", ["0", "1.5"])
+def test_two_pass_fallback(monkeypatch, headroom):
+    """Headroom forced small from the host: segments whose max grows past it
+    are redone as an exact max pass + accumulation pass."""
+    mla = need_gpu()
+    monkeypatch.setenv("MLA_ATTEND_HEADROOM", headroom)
+    wl = replace(synth.TINY, grid_hw=(30, 10), query_frames=(6,), cache_frames=tuple(range(6)))
+    inp = synth.attend_inputs(wl, seed=13)
+    want = _oracle(wl, inp)
+    assert_g1(_gpu(mla, wl, inp), want, "two-pass bf16")
+    assert_g2(_gpu(mla, wl, inp, out_dtype=torch.float32), want, "two-pass f32 out")
