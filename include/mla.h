@@ -34,9 +34,13 @@
  *   - Arguments are validated on the host before anything is enqueued; on
  *     any error nothing is enqueued and a negative mla_status is returned.
  *     mla_last_error() gives a human-readable reason (thread-local).
- *   - The library keeps no global mutable state apart from a per-device cache
- *     of the compute-unit count; calls are thread-safe.  Calls that share a
- *     workspace must be ordered on one stream.
+ *   - The library keeps no global mutable state; calls are thread-safe.
+ *     Calls that share a workspace must be ordered on one stream.
+ *   - MLA_ATTEND_HEADROOM (read at each call; default 32, range 0..64) sets how
+ *     far, in log2 units, scores may rise above a key segment's first-block
+ *     maximum before that segment is redone as an exact two-pass softmax.  It
+ *     changes rounding only, never the result beyond it; tests lower it to
+ *     exercise the two-pass path.
  *   - dtype MLA_BF16 means every floating-point input of the call is bfloat16;
  *     MLA_F32 means every one is float32.  Positions are always int32.
  *
@@ -98,7 +102,7 @@ typedef struct mla_dims {
  *            other slots are untouched.
  * Each output value is accumulated in fp32 from the dtype inputs, rotated in
  * fp32 with fp64-evaluated angles, and rounded once (to nearest even when the
- * dtype is bf16).  Requires d_model % 32 == 0 (bf16), n_new >= 0,
+ * dtype is bf16).  Requires d_model % 64 == 0 (bf16), n_new >= 0,
  * 0 <= write_offset, write_offset + n_new <= cache_capacity.  n_new == 0 is a
  * no-op returning MLA_OK. */
 int32_t mla_cache_append(const mla_dims* dims, int32_t dtype,

@@ -145,8 +145,8 @@ int32_t mla_cache_append(const mla_dims* dims, int32_t dtype, const void* x, int
   if ((st = check_dtype(dtype, "dtype"))) return st;
   if (n_new < 0) return fail(MLA_ERR_INVALID_ARG, "n_new must be >= 0");
   if (d_model < 1) return fail(MLA_ERR_INVALID_ARG, "d_model must be >= 1");
-  if (dtype == MLA_BF16 && d_model % 32 != 0)
-    return fail(MLA_ERR_UNSUPPORTED, "d_model must be a multiple of 32 for bf16 (got %d)", d_model);
+  if (dtype == MLA_BF16 && d_model % 64 != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "d_model must be a multiple of 64 for bf16 (got %d)", d_model);
   if (cache_capacity < 1 || write_offset < 0 || (int64_t)write_offset + n_new > cache_capacity)
     return fail(MLA_ERR_INVALID_ARG, "write_offset %d + n_new %d exceeds cache_capacity %d", write_offset, n_new,
                 cache_capacity);

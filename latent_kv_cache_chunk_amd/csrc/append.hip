@@ -12,73 +12,97 @@ namespace mla {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// One wavefront computes 32 tokens x all (d_c + d_r) outputs with bf16 MFMA
-// 32x32x16, fp32 accumulation.  The product is formed transposed,
-// C^T[n][token] = sum_k W[n][k] x[token][k], so each lane ends up holding
-// four consecutive outputs of one token: RoPE pairs are lane-local and the
-// bf16 store is 8 bytes.  Weight rows (n) are the A operand and are read
-// straight from global memory (they stay in L2, the whole [W_DKV; W_KR] is
-// 688 KB at D = 1536, d_c = 192); hidden states are the B operand.
+// One workgroup computes 32 tokens x all (d_c + d_r) outputs with bf16 MFMA
+// 32x32x16 and fp32 accumulation.  Its four wavefronts split the reduction
+// over d_model (a quarter each, loads issued four k-steps ahead) and their
+// fp32 partial sums are added in LDS, in a fixed order.  The product is formed
+// transposed, C^T[n][token] = sum_k W[n][k] x[token][k]: weight rows (n) are
+// the A operand, read from global memory (the whole [W_DKV; W_KR] is 688 KB at
+// D = 1536, d_c = 192, and stays in L2), hidden states are the B operand.  In
+// the epilogue each thread owns four consecutive outputs of one token, so the
+// RoPE pairs are thread-local and the store is 8 bytes.
 template <int NB>
-__global__ __launch_bounds__(64)
+__global__ __launch_bounds__(256)
 void append_bf16_kernel(const u16* __restrict__ x, int D, int ntok, int n_new,
                         const u16* __restrict__ w_dkv, const u16* __restrict__ w_kr, int d_c,
                         const int* __restrict__ pos, u16* __restrict__ cache, int cap, int off,
                         RopeSpec rope) {
   constexpr int W = NB * 32;
-  const int lane = threadIdx.x;
-  const int half = lane >> 5;
-  const int my_tok = blockIdx.x * 32 + (lane & 31);
-  const bool tok_ok = my_tok < ntok;
-  const u16* xrow = x + (int64_t)(tok_ok ? my_tok : 0) * D + half * 8;
+  constexpr int UNROLL = 4;
+  __shared__ float part[4][32][W + 4];     // per-wave partial sums [token][n]
 
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tok0 = blockIdx.x * 32;
+  const int my_tok = tok0 + (lane & 31);
+  const bool tok_ok = my_tok < ntok;
+  const int kq = D / 4;                                  // this wave's share of the reduction
+  const int kbeg = wave * kq;
+  const u16* xrow = x + (int64_t)(tok_ok ? my_tok : 0) * D + kbeg + half * 8;
   const u16* wrow[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n = nb * 32 + (lane & 31);
-    wrow[nb] = (n < d_c ? w_dkv + (int64_t)n * D : w_kr + (int64_t)(n - d_c) * D) + half * 8;
+    wrow[nb] = (n < d_c ? w_dkv + (int64_t)n * D : w_kr + (int64_t)(n - d_c) * D) + kbeg + half * 8;
   }
 
   f32x16 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
-
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int k = 0; k < D; k += 16) {
-    const bf16x8 bx = tok_ok ? *reinterpret_cast<const bf16x8*>(xrow + k)
-                             : __builtin_bit_cast(bf16x8, zero);
+  const int ksteps = kq / 16;
+  int k = 0;
+  for (; k + UNROLL <= ksteps; k += UNROLL) {
+    bf16x8 bx[UNROLL], aw[UNROLL][NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const bf16x8 aw = *reinterpret_cast<const bf16x8*>(wrow[nb] + k);
-      acc[nb] = mfma_32x32x16(aw, bx, acc[nb]);
+    for (int u = 0; u < UNROLL; ++u) {
+      bx[u] = tok_ok ? *reinterpret_cast<const bf16x8*>(xrow + (k + u) * 16) : __builtin_bit_cast(bf16x8, zero);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) aw[u][nb] = *reinterpret_cast<const bf16x8*>(wrow[nb] + (k + u) * 16);
     }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_32x32x16(aw[u][nb], bx[u], acc[nb]);
   }
-  if (!tok_ok) return;
+  for (; k < ksteps; ++k) {
+    const bf16x8 bx = tok_ok ? *reinterpret_cast<const bf16x8*>(xrow + k * 16) : __builtin_bit_cast(bf16x8, zero);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      acc[nb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(wrow[nb] + k * 16), bx, acc[nb]);
+  }
+  // partial sums -> LDS: lane holds token (lane & 31), outputs nb*32 + 8g + 4*half + t
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<f32x4*>(&part[wave][lane & 31][nb * 32 + g * 8 + half * 4]) =
+          f32x4{acc[nb][4 * g], acc[nb][4 * g + 1], acc[nb][4 * g + 2], acc[nb][4 * g + 3]};
+  __syncthreads();
 
-  const int b = my_tok / n_new, i = my_tok - b * n_new;
-  u16* dst = cache + ((int64_t)b * cap + off + i) * W;
-  const int pt = pos[3 * i + 0], ph = pos[3 * i + 1], pw = pos[3 * i + 2];
+  // epilogue: each thread takes groups of 4 consecutive outputs of one token
+  constexpr int GROUPS = 32 * W / 4;
+  for (int gi = tid; gi < GROUPS; gi += 256) {
+    const int t = gi / (W / 4), n0 = (gi - t * (W / 4)) * 4;
+    const int tok = tok0 + t;
+    if (tok >= ntok) continue;
+    f32x4 v = *reinterpret_cast<const f32x4*>(&part[0][t][n0]);
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int n0 = nb * 32 + g * 8 + half * 4;       // 4 consecutive outputs
-      float v0 = acc[nb][4 * g + 0], v1 = acc[nb][4 * g + 1];
-      float v2 = acc[nb][4 * g + 2], v3 = acc[nb][4 * g + 3];
-      if (n0 >= d_c) {                                  // positional key: rotate pairs
-        const int pair = (n0 - d_c) >> 1;
-        const double a0 = rope_angle(pair, pt, ph, pw, rope);
-        const double a1 = rope_angle(pair + 1, pt, ph, pw, rope);
-        const float c0 = (float)cos(a0), s0 = (float)sin(a0);
-        const float c1 = (float)cos(a1), s1 = (float)sin(a1);
-        const float r0 = fmaf(v0, c0, -(v1 * s0)), r1 = fmaf(v0, s0, v1 * c0);
-        const float r2 = fmaf(v2, c1, -(v3 * s1)), r3 = fmaf(v2, s1, v3 * c1);
-        v0 = r0; v1 = r1; v2 = r2; v3 = r3;
-      }
-      const uint32_t lo = bf16x2_bits(to_bf16x2(v0, v1));
-      const uint32_t hi = bf16x2_bits(to_bf16x2(v2, v3));
-      *reinterpret_cast<uint2*>(dst + n0) = make_uint2(lo, hi);
+    for (int w2 = 1; w2 < 4; ++w2) v += *reinterpret_cast<const f32x4*>(&part[w2][t][n0]);
+    const int b = tok / n_new, i = tok - b * n_new;
+    if (n0 >= d_c) {                                   // positional key: rotate the two pairs
+      const int pt = pos[3 * i], ph = pos[3 * i + 1], pw = pos[3 * i + 2];
+      const int pair = (n0 - d_c) >> 1;
+      const double a0 = rope_angle(pair, pt, ph, pw, rope);
+      const double a1 = rope_angle(pair + 1, pt, ph, pw, rope);
+      const float c0 = (float)cos(a0), s0 = (float)sin(a0);
+      const float c1 = (float)cos(a1), s1 = (float)sin(a1);
+      const float r0 = fmaf(v[0], c0, -(v[1] * s0)), r1 = fmaf(v[0], s0, v[1] * c0);
+      const float r2 = fmaf(v[2], c1, -(v[3] * s1)), r3 = fmaf(v[2], s1, v[3] * c1);
+      v = f32x4{r0, r1, r2, r3};
     }
+    u16* dst = cache + ((int64_t)b * cap + off + i) * W + n0;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(bf16x2_bits(to_bf16x2(v[0], v[1])), bf16x2_bits(to_bf16x2(v[2], v[3])));
   }
 }
 
@@ -116,7 +140,7 @@ void append_f32_kernel(const float* __restrict__ x, int D, int ntok, int n_new,
 
 hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s) {
   const int ntok = a.batch * a.n_new;
-  const dim3 grid((ntok + 31) / 32), block(64);
+  const dim3 grid((ntok + 31) / 32), block(256);
   const u16* x = (const u16*)a.x;
   const u16* wd = (const u16*)a.w_dkv;
   const u16* wk = (const u16*)a.w_kr;

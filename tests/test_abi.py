@@ -121,7 +121,7 @@ def test_calls_fail_validation_without_launching():
     # append: offset + n_new beyond capacity, bad d_model
     rc = lib.mla_cache_append(ctypes.byref(d), 0, fake, 1536, 48, fake, fake, fake, fake, 100, 60, None)
     assert rc == -1
-    rc = lib.mla_cache_append(ctypes.byref(d), 0, fake, 1530, 48, fake, fake, fake, fake, 100, 0, None)
+    rc = lib.mla_cache_append(ctypes.byref(d), 0, fake, 1568, 48, fake, fake, fake, fake, 100, 0, None)
     assert rc == -2
     rc = lib.mla_cache_append(ctypes.byref(d), 0, fake, 1536, -1, fake, fake, fake, fake, 100, 0, None)
     assert rc == -1
