@@ -18,7 +18,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // Rows of (batch, head, query) handled by one attention workgroup.
 constexpr int kRowsPerBlock = 256;
 // Keys per latent tile staged in LDS.
-constexpr int kKeyTile = 64;
+constexpr int kKeyTile = 128;
 // Compute units the work partition is sized for (MI355X).
 constexpr int kPartitionCUs = 256;
 // log2(e): softmax runs in base 2 with this folded into the query scale.
