@@ -114,17 +114,42 @@ struct WaveState {
 
 enum class Pass { kSingle, kMax, kAccum };
 
-// Scores of one 32-key block for the wave's row blocks.
-template <int DC, int QB>
+// Scores of one 32-key block for the wave's row blocks.  The k-steps feed two
+// independent accumulator chains per row block (summed at the end) so that
+// consecutive MFMAs never wait on each other's results, and the LDS operand
+// loads run PF k-steps ahead of the MFMA that uses them.
+template <int DC, int QB, int CHAINS = 2>
 __device__ __forceinline__ void block_scores(const WaveState<DC, QB>& st, const char* kbase, f32x16 (&s)[QB]) {
   constexpr int KS = WaveState<DC, QB>::KS;
+  constexpr int PF = 4;
+  f32x16 acc[QB][CHAINS];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int c = 0; c < CHAINS; ++c) acc[qb][c] = f32x16{};
+  bf16x8 a[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) a[i] = *reinterpret_cast<const bf16x8*>(kbase + i * 32);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbase + ks * 32);
+    const bf16x8 cur = a[ks % PF];
+    if (ks + PF < KS) a[ks % PF] = *reinterpret_cast<const bf16x8*>(kbase + (ks + PF) * 32);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) s[qb] = mfma_32x32x16(a, st.qf[qb][ks], s[qb]);
+    for (int qb = 0; qb < QB; ++qb) acc[qb][ks % CHAINS] = mfma_32x32x16(cur, st.qf[qb][ks], acc[qb][ks % CHAINS]);
+  }
+  // Issue order: PF loads, then (MFMA of step ks, load of step ks + PF).
+#pragma unroll
+  for (int i = 0; i < PF; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+    if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    s[qb] = acc[qb][0];
+#pragma unroll
+    for (int c = 1; c < CHAINS; ++c) s[qb] += acc[qb][c];
   }
 }
 
