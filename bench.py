@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA chunk-attention TFLOP/s + ms/chunk (480P, d_c=192); % bf16 MFMA peak"
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 HBM_PEAK_GBS = 8000.0
+COPY_BYTES = 1 << 30           # calibration copy of the traffic probe
 ATTEND_SOURCES = ("latent_kv_cache_chunk_amd/csrc/attend.hip", "latent_kv_cache_chunk_amd/csrc/mla_common.h")
 
 
@@ -46,7 +47,8 @@ def kernel_source_hash() -> str:
 
 
 def load_traffic(workload: str):
-    """HBM bytes per attend launch from committed rocprofv3 counters, if the kernel is unchanged."""
+    """HBM bytes per attend launch from committed rocprofv3 counters (written by
+    latent_kv_cache_chunk_amd.profile_summary), if the kernel source is unchanged."""
     path = os.path.join(ROOT, "profiles", f"attend_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -94,6 +96,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads whose rows form the oracle sample")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="for rocprofv3 --pmc runs: a plain copy of known size, then a few steps; no timing")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -136,6 +140,19 @@ def main(argv=None) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.traffic_probe:
+        # Calibration for the HBM byte counters: an elementwise kernel (negation)
+        # over COPY_BYTES reads and writes exactly that many bytes once each.
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": True, "copy_bytes": COPY_BYTES, "steps": 3, "workload": wl.name}))
+        return 0
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)

@@ -1,0 +1,144 @@
+"""Summaries of rocprofv3 output for the committed profiles.
+
+    python -m latent_kv_cache_chunk_amd.profile_summary trace <run_kernel_stats.csv> --title T --command C --out F.md
+    python -m latent_kv_cache_chunk_amd.profile_summary traffic <fetch_counter_collection.csv>
+        <write_counter_collection.csv> --workload wan480p --command-fetch C1 --command-write C2
+        --out-json profiles/attend_traffic_wan480p.json --out-md F.md
+
+`trace` turns the kernel statistics table into markdown.  `traffic` converts
+FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel into bytes,
+scaled by what the same counters read for the probe's calibration kernel (an
+elementwise negation that reads and writes a known number of bytes once),
+and records the attention source hash so a later kernel change invalidates it.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def short_name(name: str) -> str:
+    m = re.search(r"mla::(\w+<[^>]*>)", name)
+    if m:
+        return m.group(1)
+    return name.split("(")[0][-80:]
+
+
+def cmd_trace(a) -> None:
+    rows = list(csv.DictReader(open(a.stats)))
+    lines = [f"# {a.title}", "", "Command (repo root, one MI355X):", "", f"    {a.command}", ""]
+    if a.note:
+        lines += [a.note, ""]
+    lines += ["| Kernel | Calls | Avg (us) | Min (us) | Max (us) | Share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    if a.kernel_trace:
+        # mean over the timed steps only: drop each kernel's first `skip` dispatches (warmup)
+        per = defaultdict(list)
+        for r in csv.DictReader(open(a.kernel_trace)):
+            per[short_name(r["Kernel_Name"])].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        lines += ["", f"Excluding the first {a.skip} dispatches of each kernel (warmup):", "",
+                  "| Kernel | Dispatches | Avg (us) | Median (us) |", "|---|---|---|---|"]
+        for k, v in per.items():
+            v = sorted(v[a.skip:]) if len(v) > a.skip else sorted(v)
+            t = [x / 1e3 for x in v]
+            lines.append(f"| {k} | {len(t)} | {sum(t) / len(t):.1f} | {t[len(t) // 2]:.1f} |")
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _counter(path: str, counter: str):
+    """Per-kernel list of per-dispatch counter values."""
+    per = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return per
+
+
+def _pick(per, pattern: str):
+    hits = [(k, v) for k, v in per.items() if re.search(pattern, k)]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one kernel matching {pattern!r}, found {[k[:60] for k, _ in hits]}")
+    return hits[0]
+
+
+def cmd_traffic(a) -> None:
+    sys.path.insert(0, ROOT)
+    import bench
+    fetch = _counter(a.fetch, "FETCH_SIZE")
+    write = _counter(a.write, "WRITE_SIZE")
+    _, f_copy = _pick(fetch, r"neg")
+    _, w_copy = _pick(write, r"neg")
+    name, f_att = _pick(fetch, r"attend_bf16_kernel")
+    _, w_att = _pick(write, r"attend_bf16_kernel")
+    kib = 1024.0
+    copy_bytes = float(a.copy_bytes)
+    f_scale = copy_bytes / (sum(f_copy) / len(f_copy) * kib)
+    w_scale = copy_bytes / (sum(w_copy) / len(w_copy) * kib)
+    f_b = sum(f_att) / len(f_att) * kib * f_scale
+    w_b = sum(w_att) / len(w_att) * kib * w_scale
+    out = {
+        "kernel": short_name(name), "workload": a.workload,
+        "kernel_source_hash": bench.kernel_source_hash(),
+        "hbm_bytes_per_launch": round(f_b + w_b),
+        "fetch_bytes_per_launch": round(f_b), "write_bytes_per_launch": round(w_b),
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "calibration": f"elementwise negation of {int(copy_bytes)} bytes (reads and writes each once)",
+        "dispatches": {"attend": len(f_att), "copy": len(f_copy)},
+        "commands": {"fetch": a.command_fetch, "write": a.command_write},
+    }
+    json.dump(out, open(a.out_json, "w"), indent=1)
+    md = [f"# HBM traffic: {out['kernel']}, workload {a.workload}", "",
+          "Commands (repo root, one MI355X; one counter per pass):", "",
+          f"    {a.command_fetch}", f"    {a.command_write}", "",
+          f"Calibration: {out['calibration']}: FETCH_SIZE reads {sum(f_copy) / len(f_copy):.0f} KiB per dispatch "
+          f"(scale {f_scale:.4f}), WRITE_SIZE {sum(w_copy) / len(w_copy):.0f} KiB (scale {w_scale:.4f}).", "",
+          "| Counter | KiB per attend dispatch (mean) | Scaled bytes |", "|---|---|---|",
+          f"| FETCH_SIZE | {sum(f_att) / len(f_att):.0f} | {f_b / 1e9:.3f} GB |",
+          f"| WRITE_SIZE | {sum(w_att) / len(w_att):.0f} | {w_b / 1e9:.3f} GB |", "",
+          f"Total {(f_b + w_b) / 1e9:.3f} GB per launch; attention source hash {out['kernel_source_hash']}."]
+    if a.note:
+        md += ["", a.note]
+    open(a.out_md, "w").write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("stats")
+    t.add_argument("--title", required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--note", default="")
+    t.add_argument("--kernel-trace", default="", help="run_kernel_trace.csv, for the timed-steps mean")
+    t.add_argument("--skip", type=int, default=0)
+    t.add_argument("--out", required=True)
+    f = sub.add_parser("traffic")
+    f.add_argument("fetch")
+    f.add_argument("write")
+    f.add_argument("--workload", default="wan480p")
+    f.add_argument("--copy-bytes", type=int, default=1 << 30)
+    f.add_argument("--command-fetch", required=True)
+    f.add_argument("--command-write", required=True)
+    f.add_argument("--note", default="")
+    f.add_argument("--out-json", required=True)
+    f.add_argument("--out-md", required=True)
+    a = ap.parse_args(argv)
+    {"trace": cmd_trace, "traffic": cmd_traffic}[a.cmd](a)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

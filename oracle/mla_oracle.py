@@ -18,7 +18,7 @@ atlas.scime.ai summary):
   atlas.scime.ai summary, "Key results": 224 scalars per token per layer at
   d_c = 192, d_r = 32, against 3072 for 12 heads x 128 of dense K and V).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   * 3D-RoPE: the d_r vector is split into contiguous per-axis blocks
     [t | h | w] (default widths 8/12/12); inside a block of width d_a, the
     adjacent pair (2i, 2i+1) is rotated by angle p_a * theta**(-2i/d_a),
