@@ -4,373 +4,447 @@
 // visible key j (all cached chunks plus the chunk itself -- chunk-causal,
 // bidirectional inside the chunk; VideoMLA atlas.scime.ai summary, first
 // paragraph) the score is the dot product of the absorbed query q~_r with the
-// cached row [c_j || k_R,j]; the kernel keeps an online base-2 softmax and
+// cached row [c_j || k_R,j]; the kernel keeps a base-2 softmax and
 // accumulates L_r = sum_j p_rj c_j in fp32.  Every head reads the same latent
 // rows (VideoMLA arXiv abstract: one latent and one positional key shared by
 // all heads), so a workgroup packs 256 rows of any heads and streams each key
 // tile through LDS once for all of them.
 //
-// MFMA formulation (bf16 32x32x16, fp32 accumulate), per 32-row block:
-//   S^T[key][row]  = K_tile[key][:] . q~[row][:]     A = key rows (LDS, b128),
-//                                                    B = q~ rows (registers)
-//   O^T[c][row]   += V^T[c][key] . P^T[key][row]     A = latent columns read
-//                                                    transposed from the same
-//                                                    LDS tile (ds_read_tr16_b64),
-//                                                    B = P straight from S^T
-// With keys on the MFMA rows, one lane holds 16 keys of one row, so the row
-// max and row sum are lane-local plus one exchange with lane^32.  Lane-half h
-// of the S^T accumulator holds keys {8g + 4h + t}; the transposed loads fetch
-// exactly those keys for the P.V k-step, so P never moves between lanes.
+// Wavefront roles.  The 256 rows form four groups of 64.  Each group has a
+// score wavefront and a value wavefront, placed on the same SIMD:
+//   score:  S^T[key][row] = K_blk[key][:] . q~[row][:]  (bf16 MFMA 32x32x16,
+//           A = key rows read from LDS, B = q~ rows held in registers), then
+//           p = 2^(s - m) in fp32, the row sums, and P in bf16 written to LDS;
+//   value:  O^T[c][row] += V^T[c][key] . P^T[key][row]  (A = latent columns
+//           read transposed from the same LDS tile with ds_read_tr16_b64,
+//           B = P read back from LDS).
+// The score wavefront never holds O and the value wavefront never holds q~,
+// so each fits its registers with room to spare, and while one wavefront of
+// a SIMD is in its softmax the other keeps the matrix core busy.  Each LDS
+// operand read feeds two MFMAs (the group's two 32-row halves).
 //
-// Staging: each tile of kKeyTile keys is copied global -> LDS by direct-to-LDS
-// 16-byte loads (no registers), one row per key padded to an odd number of
-// 16-byte slots so b128 reads of 16 consecutive rows hit distinct banks.  Two
-// buffers: the next tile's loads are in flight while the current one is used;
-// one barrier per tile.
+// With keys on the MFMA rows one lane holds 16 keys of one row, so row sums
+// are lane-local.  Lane-half h of the S^T accumulator holds keys
+// {8g + 4h + t}; the transposed loads fetch exactly those keys for the P.V
+// k-step, so each lane's P values go to LDS and come back to the same lane
+// of the value wavefront unchanged.
 //
-// Softmax without in-loop rescaling.  The accumulators are never rescaled
-// inside the key loop (VALU work on them would force them out of the MFMA
-// accumulator registers).  Each row's reference max m is fixed by the first
-// 32-key block of a segment, and later scores may exceed it by up to
-// `headroom` in log2 units (32 by default): p = 2^(s - m) stays below
-// 2^headroom, far inside the fp32/bf16 range, and the result is the same
-// softmax (numerator and denominator share m).  If any row of a workgroup
-// exceeded the headroom anywhere in a segment (checked once, at its end), the
-// segment is redone exactly: a max-only sweep, then accumulation against the
-// true max.
+// Pipeline.  Key tiles are copied global -> LDS by direct-to-LDS 16-byte
+// loads (no registers), one row per key padded to an odd number of 16-byte
+// slots so b128 reads of 16 consecutive rows hit distinct banks.  In step k
+// the score wavefronts work on tile k, the value wavefronts on tile k-1 (with
+// the P of step k-1), and tile k+1 is in flight: three key buffers, two P
+// buffers, one barrier per step.
+//
+// Softmax without rescaling.  The accumulators are never rescaled.  Each
+// row's reference max m is fixed by the first 32-key block of a segment and
+// p = 2^(s - m) is accumulated as is: numerator and denominator share m, so
+// the softmax is unchanged.  Later keys may score above m; this is safe while
+// p stays far inside the fp32 range.  Since every p >= 0, a lane's running
+// sum bounds each of its p, so one check per segment suffices: if a lane's
+// sum exceeds 2^headroom (32 by default) or an accumulator is not finite, the
+// segment is redone exactly -- a max-only sweep, then accumulation against
+// the true max.
 #include "mla_common.h"
 #include "mla_kernels.h"
 
 namespace mla {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ inline void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0), others free
 
-template <int DC, int NW>
+constexpr int kWaves = 8;          // wavefronts per workgroup
+constexpr int kGroups = 4;         // row groups (score + value wavefront each)
+constexpr int kGroupRows = 64;     // rows per group: two 32-row MFMA blocks
+static_assert(kGroups * kGroupRows == kRowsPerBlock, "a workgroup covers one row block");
+
+template <int DC>
 struct AttendTile {
   static constexpr int W = DC + 32;          // cached row width (elements)
   static constexpr int NCH = W / 8;          // 16-byte chunks per cached row
   static constexpr int NSLOT = NCH + 1;      // plus one pad slot: stride = 4 * odd dwords
   static constexpr int ROWB = NSLOT * 16;    // LDS bytes per key row
-  static constexpr int BN = kKeyTile;        // keys per tile
+  static constexpr int BN = key_tile(DC);    // keys per tile
   static constexpr int NBLK = BN / 32;       // 32-key MFMA blocks per tile
-  static constexpr int TILEB = BN * ROWB;    // LDS bytes per tile buffer
+  static constexpr int TILEB = BN * ROWB;    // LDS bytes per key buffer
   static constexpr int ROWS_PER_LOAD = 64 / NSLOT;   // whole rows one 64-lane load copies
   static constexpr int NLOAD = (BN + ROWS_PER_LOAD - 1) / ROWS_PER_LOAD;
-  static constexpr int LOADS_PER_WAVE = (NLOAD + NW - 1) / NW;
+  static constexpr int LOADS_PER_WAVE = (NLOAD + kWaves - 1) / kWaves;
+  static constexpr int KS = W / 16;          // score k-steps
+  static constexpr int CB = DC / 32;         // 32-column latent blocks of O^T
+  static constexpr int PBLK = kGroups * 2 * 2 * 64 * 16;   // P bytes of one block: groups x halves x k-steps x lanes
+  static constexpr int PBUF = NBLK * PBLK;                 // LDS bytes per P buffer
   static_assert(ROWS_PER_LOAD >= 1, "a cached row must fit one 64-lane load");
+  static_assert(3 * TILEB + 2 * PBUF <= 160 * 1024, "buffers exceed LDS");
 };
 
 // Per-lane part of the direct-to-LDS copy: lane l copies chunk l % NSLOT of
 // row l / NSLOT of the load's rows (the pad slot re-reads the row's last
 // chunk); lanes past the last whole row stay idle (lane_row >= ROWS_PER_LOAD).
-template <int DC, int NW>
-__device__ inline int lane_copy_offset(int lane, int& lane_row) {
-  using L = AttendTile<DC, NW>;
+// Returns the chunk's byte offset inside its row.
+template <int DC>
+__device__ inline int lane_copy_chunk(int lane, int& lane_row) {
+  using L = AttendTile<DC>;
   lane_row = lane / L::NSLOT;
-  const int ch = min(lane - lane_row * L::NSLOT, L::NCH - 1);
-  return (lane_row * L::W + ch * 8) * 2;
+  return min(lane - lane_row * L::NSLOT, L::NCH - 1) * 16;
 }
 
-// Enqueue the direct-to-LDS loads of key tile [key0, key0 + BN) into `tile`.
-// Load i copies R = ROWS_PER_LOAD whole rows, [iR, iR + R), to LDS rows
-// [iR, iR + R); in the last, partial tile rows past n_k re-read key n_k-1
-// (their scores are masked).
-template <int DC, int NW>
-__device__ inline void issue_tile(const char* gbase, int key0, int n_k, char* tile, int wave, int lane_off,
-                                  int lane_row) {
-  using L = AttendTile<DC, NW>;
-  const bool partial = key0 + L::BN > n_k;
+// Wave-invariant addressing of one sweep.
+struct SweepCtx {
+  const char* gbase;   // cache rows of this sample
+  int n_k;
+  int wave, lane, half, group;
+  int lane_chunk, lane_row;
+  int s_off;           // b128 score operand offset inside a block
+  int v_off;           // transposed latent operand offset inside a block
+};
+
+// Enqueue this wavefront's share of the direct-to-LDS loads of key tile t
+// into `tile`.  Load i copies R = ROWS_PER_LOAD whole rows, [iR, iR + R), to
+// LDS rows [iR, iR + R); in the last, partial tile rows past n_k re-read key
+// n_k-1 (their scores are masked).  Source addresses are the sample's base
+// plus a 32-bit unsigned offset (a sample's cache is below 4 GiB).
+template <int DC>
+__device__ inline void issue_tile(const SweepCtx& c, int t, char* tile) {
+  using L = AttendTile<DC>;
+  const int key0 = t * L::BN;
 #pragma unroll
   for (int i = 0; i < L::LOADS_PER_WAVE; ++i) {
-    const int ld = wave + NW * i;
+    const int ld = c.wave + kWaves * i;
     if (ld < L::NLOAD) {
       const int row0 = ld * L::ROWS_PER_LOAD;
-      const char* src = gbase + (int64_t)(key0 + row0) * (L::W * 2);
-      int o = lane_off;
-      if (partial) {
-        const int key = key0 + row0 + lane_row;
-        o += (min(key, n_k - 1) - key) * (L::W * 2);
-      }
-      if (lane_row < L::ROWS_PER_LOAD && row0 + lane_row < L::BN)
-        __builtin_amdgcn_global_load_lds(src + o, (lds_void*)(tile + row0 * L::ROWB), 16, 0, 0);
+      const uint32_t key = (uint32_t)min(key0 + row0 + c.lane_row, c.n_k - 1);
+      const uint32_t off = key * (uint32_t)(L::W * 2) + (uint32_t)c.lane_chunk;
+      if (c.lane_row < L::ROWS_PER_LOAD && row0 + c.lane_row < L::BN)
+        __builtin_amdgcn_global_load_lds(c.gbase + off, (lds_void*)(tile + row0 * L::ROWB), 16, 0, 0);
     }
   }
 }
-
-// Softmax state of one wavefront: QB 32-row MFMA blocks.
-template <int DC, int QB>
-struct WaveState {
-  static constexpr int KS = (DC + 32) / 16, CB = DC / 32;
-  bf16x8 qf[QB][KS];     // absorbed queries, MFMA B operands
-  f32x16 oacc[QB][CB];   // O^T accumulators (latent columns x rows)
-  float m_ref[QB];       // reference max (base 2), identical in lanes l and l^32
-  float l_run[QB];       // this lane's part of the running sum
-};
 
 enum class Pass { kSingle, kMax, kAccum };
 
-// Scores of one 32-key block for the wave's row blocks.  The k-steps feed two
-// independent accumulator chains per row block (summed at the end) so that
-// consecutive MFMAs never wait on each other's results, and the LDS operand
-// loads run PF k-steps ahead of the MFMA that uses them.
-template <int DC, int QB, int CHAINS = 2>
-__device__ __forceinline__ void block_scores(const WaveState<DC, QB>& st, const char* kbase, f32x16 (&s)[QB]) {
-  constexpr int KS = WaveState<DC, QB>::KS;
-  constexpr int PF = 4;
-  f32x16 acc[QB][CHAINS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int c = 0; c < CHAINS; ++c) acc[qb][c] = f32x16{};
-  bf16x8 a[PF];
-#pragma unroll
-  for (int i = 0; i < PF; ++i) a[i] = *reinterpret_cast<const bf16x8*>(kbase + i * 32);
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const bf16x8 cur = a[ks % PF];
-    if (ks + PF < KS) a[ks % PF] = *reinterpret_cast<const bf16x8*>(kbase + (ks + PF) * 32);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) acc[qb][ks % CHAINS] = mfma_32x32x16(cur, st.qf[qb][ks], acc[qb][ks % CHAINS]);
-  }
-  // Issue order: PF loads, then (MFMA of step ks, load of step ks + PF).
-#pragma unroll
-  for (int i = 0; i < PF; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
-    if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    s[qb] = acc[qb][0];
-#pragma unroll
-    for (int c = 1; c < CHAINS; ++c) s[qb] += acc[qb][c];
-  }
+// Byte offset of lane `lane`'s 16-byte P operand (row half qb, k-step part)
+// of group g inside one block of a P buffer.
+__device__ __forceinline__ int p_slot(int g, int qb, int part, int lane) {
+  return (((g * 2 + qb) * 2 + part) * 64 + lane) * 16;
 }
 
-// Softmax of one 32-key block: scores s (base-2 logits, masked keys = -inf)
-// -> bf16 P operands.  kMax only raises the reference max.  kSingle fixes the
-// reference max at the segment's first block and flags rows that exceed it by
-// more than `headroom`.
-template <int DC, int QB, Pass P>
-__device__ __forceinline__ void block_softmax(WaveState<DC, QB>& st, f32x16 (&s)[QB], bf16x8 (&pb)[QB][2],
-                                              bool first_block, float headroom, bool& over) {
+// Keys of the block at or past n_valid get score -inf (p = 0).  Value v of
+// lane-half h is key (v>>2)*8 + 4h + (v&3) of the block.
+__device__ __forceinline__ void mask_block(f32x16& s, int n_valid, int half) {
+  const int thr = n_valid - half * 4;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    if (P != Pass::kAccum) {
-      float mx = s[qb][0];
+  for (int v = 0; v < 16; ++v)
+    if ((v >> 2) * 8 + (v & 3) >= thr) s[v] = -INFINITY;
+}
+
+// Row max of a block (both lane halves).
+__device__ __forceinline__ float block_max(const f32x16& s) {
+  const float a = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  const float b = fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]));
+  const float c = fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11]));
+  const float d = fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]));
+  const float m = fmaxf(fmaxf(a, b), fmaxf(c, d));
+  return fmaxf(m, __shfl_xor(m, 32));
+}
+
+// ---------------------------------------------------------------- score role
+template <int DC>
+struct ScoreState {
+  bf16x8 qf[2][AttendTile<DC>::KS];   // absorbed queries of the group's two halves (MFMA B operands)
+  float m_ref[2];                     // reference max (base 2), identical in lanes l and l^32
+  float l_run[2];                     // this lane's part of the running sum
+};
+
+constexpr int kScorePrefetch = 4;     // score operand loads in flight ahead of their MFMAs
+
+// Scores, softmax and P of every block of tile t (LDS `tile`), P to `pbuf`.
+template <int DC, Pass P>
+__device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile, char* pbuf, int t, bool first_tile,
+                                           const SweepCtx& c) {
+  using L = AttendTile<DC>;
+  constexpr int KS = L::KS, PF = kScorePrefetch;
+  const int left = c.n_k - t * L::BN;
 #pragma unroll
-      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[qb][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+  for (int kb = 0; kb < L::NBLK; ++kb) {
+    if (kb > 0 && kb * 32 >= left) break;
+    const char* kbase = tile + kb * 32 * L::ROWB + c.s_off;
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    bf16x8 a[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) a[i] = *reinterpret_cast<const bf16x8*>(kbase + i * 32);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 cur = a[ks % PF];
+      if (ks + PF < KS) a[ks % PF] = *reinterpret_cast<const bf16x8*>(kbase + (ks + PF) * 32);
+      s[0] = mfma_32x32x16(cur, st.qf[0][ks], s[0]);
+      s[1] = mfma_32x32x16(cur, st.qf[1][ks], s[1]);
+    }
+    if (left - kb * 32 < 32) {
+      mask_block(s[0], left - kb * 32, c.half);
+      mask_block(s[1], left - kb * 32, c.half);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
       if (P == Pass::kMax) {
-        st.m_ref[qb] = fmaxf(st.m_ref[qb], mx);
+        st.m_ref[qb] = fmaxf(st.m_ref[qb], block_max(s[qb]));
         continue;
       }
-      st.m_ref[qb] = first_block ? mx : st.m_ref[qb];
-      over |= mx > st.m_ref[qb] + headroom;
-    }
-    const float m = st.m_ref[qb];
-    float lsum = 0.f;
+      if (P == Pass::kSingle && first_tile && kb == 0) st.m_ref[qb] = block_max(s[qb]);
+      const float m = st.m_ref[qb];
+      float p[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p = __builtin_amdgcn_exp2f(s[qb][v] - m);
-      s[qb][v] = p;
-      lsum += p;
+      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(s[qb][v] - m);
+      float q[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) q[v] = p[2 * v] + p[2 * v + 1];
+      st.l_run[qb] += ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        bf16x8 pv;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 two = to_bf16x2(p[part * 8 + e], p[part * 8 + e + 1]);
+          pv[e] = two[0];
+          pv[e + 1] = two[1];
+        }
+        *reinterpret_cast<bf16x8*>(pbuf + kb * L::PBLK + p_slot(c.group, qb, part, c.lane)) = pv;
+      }
     }
-    st.l_run[qb] += lsum;
+  }
+}
+
+// ---------------------------------------------------------------- value role
+template <int DC>
+struct ValueState {
+  f32x16 oacc[2][AttendTile<DC>::CB];   // O^T accumulators of the group's two halves
+};
+
+// P.V of every block of tile t (LDS `tile`), P from `pbuf`.
+template <int DC>
+__device__ __forceinline__ void value_tile(ValueState<DC>& st, const char* tile, const char* pbuf, int t,
+                                           const SweepCtx& c) {
+  using L = AttendTile<DC>;
+  const int left = c.n_k - t * L::BN;
+#pragma unroll
+  for (int kb = 0; kb < L::NBLK; ++kb) {
+    if (kb > 0 && kb * 32 >= left) break;
+    const char* pb = pbuf + kb * L::PBLK;
+    const char* blk = tile + kb * 32 * L::ROWB + c.v_off;
 #pragma unroll
     for (int part = 0; part < 2; ++part) {
-      bf16x8 pv;
+      const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(pb + p_slot(c.group, 0, part, c.lane));
+      const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(pb + p_slot(c.group, 1, part, c.lane));
+      const char* vbase = blk + part * 16 * L::ROWB;
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2 two = to_bf16x2(s[qb][part * 8 + e], s[qb][part * 8 + e + 1]);
-        pv[e] = two[0];
-        pv[e + 1] = two[1];
+      for (int cb = 0; cb < L::CB; ++cb) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + cb * 64));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + 8 * L::ROWB + cb * 64));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        st.oacc[0][cb] = mfma_32x32x16(a, p0, st.oacc[0][cb]);
+        st.oacc[1][cb] = mfma_32x32x16(a, p1, st.oacc[1][cb]);
       }
-      pb[qb][part] = pv;
     }
   }
 }
 
-// O^T += V^T P^T for one 32-key block; V^T is read transposed from the tile.
-template <int DC, int QB, int ROWB>
-__device__ __forceinline__ void block_pv(WaveState<DC, QB>& st, const char* block_row0, int v_off,
-                                         const bf16x8 (&pb)[QB][2]) {
-  constexpr int CB = WaveState<DC, QB>::CB;
-#pragma unroll
-  for (int part = 0; part < 2; ++part) {
-    const char* vbase = block_row0 + part * 16 * ROWB + v_off;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + cb * 64));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + 8 * ROWB + cb * 64));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) st.oacc[qb][cb] = mfma_32x32x16(a, pb[qb][part], st.oacc[qb][cb]);
-    }
+// ------------------------------------------------------------------ sweeps
+// One step of a segment's sweep: start tile k+1 into `nxt`, do this role's
+// work (score: tile k in `cur`, P to P[k % 2]; value: tile k-1 in `prv`, P
+// from P[(k-1) % 2]), then wait for the loads and barrier.  Steps run
+// k = 0 .. n (n tiles); returns true after step n.
+template <int DC, Pass P, bool SCORE, class State>
+__device__ __forceinline__ bool sweep_step(State& st, int k, int n, int t0, char* cur, char* nxt, char* prv,
+                                           char* pb0, char* pb1, const SweepCtx& c) {
+  if (k + 1 < n) issue_tile<DC>(c, t0 + k + 1, nxt);
+  if constexpr (SCORE) {
+    if (k < n) score_tile<DC, P>(st, cur, (k & 1) ? pb1 : pb0, t0 + k, k == 0, c);
+  } else {
+    if (P != Pass::kMax && k >= 1) value_tile<DC>(st, prv, (k & 1) ? pb0 : pb1, t0 + k - 1, c);
   }
+  wait_vmcnt0();
+  __syncthreads();
+  return k >= n;
 }
 
-// One staged tile, block by block (scores, softmax, P.V).  `left` = keys of
-// the tile that exist; blocks past it are skipped, keys past it masked.
-template <int DC, int QB, int NW, Pass P>
-__device__ __forceinline__ void attend_tile(WaveState<DC, QB>& st, const char* tile, int left, int s_off,
-                                            int v_off, int half, bool first_tile, float headroom, bool& over) {
-  using L = AttendTile<DC, NW>;
-  constexpr int ROWB = L::ROWB;
-#pragma unroll 1
-  for (int kb = 0; kb < L::NBLK; ++kb) {
-    const int n_valid = min(32, left - kb * 32);
-    if (n_valid <= 0) break;
-    f32x16 s[QB];
-    bf16x8 pb[QB][2];
-    block_scores<DC, QB>(st, tile + kb * 32 * ROWB + s_off, s);
-    if (n_valid < 32) {
-      const int thr = n_valid - half * 4;   // value v is key (v>>2)*8 + (v&3) + 4*half of the block
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if ((v >> 2) * 8 + (v & 3) >= thr) s[qb][v] = -INFINITY;
-    }
-    block_softmax<DC, QB, P>(st, s, pb, first_tile && kb == 0, headroom, over);
-    if (P != Pass::kMax) block_pv<DC, QB, ROWB>(st, tile + kb * 32 * ROWB, v_off, pb);
-  }
-}
-
-// Sweep tiles [t0, t1) of one segment through the two LDS buffers (each
-// buffer a distinct LDS object, so that reads of one tile are not ordered
-// behind the in-flight direct loads of the other).  kSingle returns true,
-// identically in every wave, if some row exceeded the headroom.
-template <int DC, int QB, int NW, Pass P>
-__device__ __forceinline__ bool sweep(WaveState<DC, QB>& st, char* sbuf0, char* sbuf1, const char* gbase, int t0,
-                                      int t1, int n_k, int wave, int lane_off, int lane_row, int s_off, int v_off,
-                                      int half, float headroom) {
-  using L = AttendTile<DC, NW>;
-  constexpr int BN = L::BN;
-  bool over = false;
-  issue_tile<DC, NW>(gbase, t0 * BN, n_k, sbuf0, wave, lane_off, lane_row);
+// Tiles [t0, t1) of one segment.  The three key buffers are distinct LDS
+// objects and each step names them statically (the loop is unrolled by
+// three), so reads of one are not ordered behind the in-flight direct loads
+// of another.  Score and value wavefronts run the same steps and barriers.
+template <int DC, Pass P, bool SCORE, class State>
+__device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* k2, char* pb0, char* pb1, int t0, int t1,
+                                      const SweepCtx& c) {
+  const int n = t1 - t0;
+  issue_tile<DC>(c, t0, k0);
   wait_vmcnt0();
   __syncthreads();
 #pragma unroll 1
-  for (int t = t0; t < t1; t += 2) {
-    // tile t is in sbuf0; tile t+1 goes to sbuf1
-    if (t + 1 < t1) issue_tile<DC, NW>(gbase, (t + 1) * BN, n_k, sbuf1, wave, lane_off, lane_row);
-    attend_tile<DC, QB, NW, P>(st, sbuf0, n_k - t * BN, s_off, v_off, half, t == t0, headroom, over);
-    wait_vmcnt0();
-    __syncthreads();
-    if (t + 1 >= t1) break;
-    if (t + 2 < t1) issue_tile<DC, NW>(gbase, (t + 2) * BN, n_k, sbuf0, wave, lane_off, lane_row);
-    attend_tile<DC, QB, NW, P>(st, sbuf1, n_k - (t + 1) * BN, s_off, v_off, half, false, headroom, over);
-    wait_vmcnt0();
-    __syncthreads();
-  }
-  return P == Pass::kSingle ? __syncthreads_or(over) : false;
-}
-
-template <int DC, int QB>
-__device__ __forceinline__ void reset_acc(WaveState<DC, QB>& st) {
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-    for (int cb = 0; cb < WaveState<DC, QB>::CB; ++cb) st.oacc[qb][cb] = f32x16{};
-    st.l_run[qb] = 0.f;
+  for (int k = 0;; k += 3) {
+    if (sweep_step<DC, P, SCORE>(st, k, n, t0, k0, k1, k2, pb0, pb1, c)) break;
+    if (sweep_step<DC, P, SCORE>(st, k + 1, n, t0, k1, k2, k0, pb0, pb1, c)) break;
+    if (sweep_step<DC, P, SCORE>(st, k + 2, n, t0, k2, k0, k1, pb0, pb1, c)) break;
   }
 }
 
-// QB = 32-row MFMA blocks per wavefront: QB = 1 -> 8 wavefronts of 32 rows
-// (two per SIMD, so one wave's softmax overlaps the other's MFMAs), QB = 2 ->
-// 4 wavefronts of 64 rows (one per SIMD, half the LDS reads per flop).
-template <int DC, int QB>
-__global__ __launch_bounds__(512 / QB, 1)
-void attend_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstride, int n_k,
-                        const u16* __restrict__ qt, int rows_pad_b, int rb_per_b,
-                        float* __restrict__ part_L, float* __restrict__ part_ml,
-                        int T, int64_t U, int G, float headroom) {
-  constexpr int NW = 8 / QB;   // wavefronts per workgroup
-  using L = AttendTile<DC, NW>;
-  constexpr int W = L::W, KS = WaveState<DC, QB>::KS, CB = WaveState<DC, QB>::CB, ROWB = L::ROWB;
-  static_assert(NW * QB * 32 == kRowsPerBlock, "a workgroup covers one row block");
+// Segments of workgroup w: contiguous (row-block, key-tile) unit ranges, at
+// most two row blocks.
+struct SegmentIter {
+  int64_t u, u_end;
+  int T, rb_per_b;
+  int64_t rb;
+  int t0, t1, b, rbl;
+  __device__ bool next() {
+    if (u >= u_end) return false;
+    rb = u / T;
+    t0 = (int)(u - rb * T);
+    t1 = (int)min<int64_t>((int64_t)T, (int64_t)t0 + (u_end - u));
+    b = (int)(rb / rb_per_b);
+    rbl = (int)(rb - (int64_t)b * rb_per_b);
+    u += (t1 - t0);
+    return true;
+  }
+};
 
-  __shared__ __attribute__((aligned(1024))) char sbuf0[L::TILEB];
-  __shared__ __attribute__((aligned(1024))) char sbuf1[L::TILEB];
-
-  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int lane_row;
-  const int lane_off = lane_copy_offset<DC, NW>(lane, lane_row);
-  // per-lane LDS offsets: b128 score operand, transposed latent operand
-  const int s_off = (lane & 31) * ROWB + half * 16;
-  const int g = lane >> 4, j = lane & 15;
-  const int v_off = ((g >> 1) * 4 + (j >> 2)) * ROWB + (16 * (g & 1) + 4 * (j & 3)) * 2;
-
-  const int64_t w = blockIdx.x;
-  int64_t u = unit_begin(w, U, G);
-  const int64_t u_end = unit_begin(w + 1, U, G);
+template <int DC>
+__device__ __forceinline__ void score_role(SweepCtx& c, SegmentIter it, const u16* __restrict__ cache,
+                                           int64_t cache_bstride, const u16* __restrict__ qt, int rows_pad_b,
+                                           float* __restrict__ part_ml, int64_t w, float headroom, char* k0,
+                                           char* k1, char* k2, char* pb0, char* pb1) {
+  using L = AttendTile<DC>;
+  ScoreState<DC> st;
   bool first_seg = true;
-  WaveState<DC, QB> st;
-
-  while (u < u_end) {
-    const int64_t rb = u / T;
-    const int t0 = (int)(u - rb * T);
-    const int t1 = (int)min<int64_t>((int64_t)T, (int64_t)t0 + (u_end - u));
-    const int b = (int)(rb / rb_per_b);
-    const int rbl = (int)(rb - (int64_t)b * rb_per_b);
-    const char* gbase = reinterpret_cast<const char*>(cache + (int64_t)b * cache_bstride);
-
-    {
-      const int64_t row0 = (int64_t)b * rows_pad_b + (int64_t)rbl * kRowsPerBlock + wave * 32 * QB;
+  while (it.next()) {
+    c.gbase = reinterpret_cast<const char*>(cache + (int64_t)it.b * cache_bstride);
+    const int64_t row0 = (int64_t)it.b * rows_pad_b + (int64_t)it.rbl * kRowsPerBlock + c.group * kGroupRows;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const u16* qrow = qt + (row0 + qb * 32 + (lane & 31)) * W + half * 8;
+    for (int qb = 0; qb < 2; ++qb) {
+      const u16* qrow = qt + (row0 + qb * 32 + (c.lane & 31)) * L::W + c.half * 8;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) st.qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
-      }
+      for (int ks = 0; ks < L::KS; ++ks) st.qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
+      st.l_run[qb] = 0.f;
     }
-    reset_acc<DC, QB>(st);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) st.m_ref[qb] = -INFINITY;
-    if (sweep<DC, QB, NW, Pass::kSingle>(st, sbuf0, sbuf1, gbase, t0, t1, n_k, wave, lane_off, lane_row, s_off,
-                                         v_off, half, headroom)) {
-      // Some score rose more than the headroom above its first-block max:
-      // exact two-pass evaluation of this segment.
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) st.m_ref[qb] = -INFINITY;
-      sweep<DC, QB, NW, Pass::kMax>(st, sbuf0, sbuf1, gbase, t0, t1, n_k, wave, lane_off, lane_row, s_off, v_off,
-                                    half, headroom);
-      reset_acc<DC, QB>(st);
-      sweep<DC, QB, NW, Pass::kAccum>(st, sbuf0, sbuf1, gbase, t0, t1, n_k, wave, lane_off, lane_row, s_off,
-                                      v_off, half, headroom);
+    sweep<DC, Pass::kSingle, true>(st, k0, k1, k2, pb0, pb1, it.t0, it.t1, c);
+    const float lim = __builtin_amdgcn_exp2f(headroom);
+    const bool over = !(st.l_run[0] <= lim) || !(st.l_run[1] <= lim);
+    if (__syncthreads_or(over)) {
+      // A running sum rose past 2^headroom: exact two-pass evaluation.
+      st.m_ref[0] = st.m_ref[1] = -INFINITY;
+      sweep<DC, Pass::kMax, true>(st, k0, k1, k2, pb0, pb1, it.t0, it.t1, c);
+      st.l_run[0] = st.l_run[1] = 0.f;
+      sweep<DC, Pass::kAccum, true>(st, k0, k1, k2, pb0, pb1, it.t0, it.t1, c);
     }
-
-    // ---- write this segment's partial softmax state
     const int64_t slot = 2 * w + (first_seg ? 0 : 1);
     first_seg = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    for (int qb = 0; qb < 2; ++qb) {
       const float l_tot = st.l_run[qb] + __shfl_xor(st.l_run[qb], 32);
-      const int rl = wave * 32 * QB + qb * 32 + (lane & 31);
-      float* Ld = part_L + (slot * kRowsPerBlock + rl) * DC;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const int c0 = cb * 32 + gg * 8 + half * 4;
-          *reinterpret_cast<f32x4*>(Ld + c0) = f32x4{st.oacc[qb][cb][4 * gg], st.oacc[qb][cb][4 * gg + 1],
-                                                     st.oacc[qb][cb][4 * gg + 2], st.oacc[qb][cb][4 * gg + 3]};
-        }
-      if (half == 0) {
+      const int rl = c.group * kGroupRows + qb * 32 + (c.lane & 31);
+      if (c.half == 0) {
         part_ml[(slot * kRowsPerBlock + rl) * 2 + 0] = st.m_ref[qb];
         part_ml[(slot * kRowsPerBlock + rl) * 2 + 1] = l_tot;
       }
     }
-    u += (t1 - t0);
   }
+}
+
+template <int DC>
+__device__ __forceinline__ void value_role(SweepCtx& c, SegmentIter it, const u16* __restrict__ cache,
+                                           int64_t cache_bstride, float* __restrict__ part_L, int64_t w, char* k0,
+                                           char* k1, char* k2, char* pb0, char* pb1) {
+  using L = AttendTile<DC>;
+  ValueState<DC> st;
+  bool first_seg = true;
+  while (it.next()) {
+    c.gbase = reinterpret_cast<const char*>(cache + (int64_t)it.b * cache_bstride);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int cb = 0; cb < L::CB; ++cb) st.oacc[qb][cb] = f32x16{};
+    sweep<DC, Pass::kSingle, false>(st, k0, k1, k2, pb0, pb1, it.t0, it.t1, c);
+    bool bad = false;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int cb = 0; cb < L::CB; ++cb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) bad |= !(fabsf(st.oacc[qb][cb][v]) <= 3.0e38f);
+    if (__syncthreads_or(bad)) {
+      sweep<DC, Pass::kMax, false>(st, k0, k1, k2, pb0, pb1, it.t0, it.t1, c);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int cb = 0; cb < L::CB; ++cb) st.oacc[qb][cb] = f32x16{};
+      sweep<DC, Pass::kAccum, false>(st, k0, k1, k2, pb0, pb1, it.t0, it.t1, c);
+    }
+    const int64_t slot = 2 * w + (first_seg ? 0 : 1);
+    first_seg = false;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int rl = c.group * kGroupRows + qb * 32 + (c.lane & 31);
+      float* Ld = part_L + (slot * kRowsPerBlock + rl) * DC;
+#pragma unroll
+      for (int cb = 0; cb < L::CB; ++cb)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int c0 = cb * 32 + gg * 8 + c.half * 4;
+          *reinterpret_cast<f32x4*>(Ld + c0) = f32x4{st.oacc[qb][cb][4 * gg], st.oacc[qb][cb][4 * gg + 1],
+                                                     st.oacc[qb][cb][4 * gg + 2], st.oacc[qb][cb][4 * gg + 3]};
+        }
+    }
+  }
+}
+
+#ifndef MLA_ATTEND_SCORE_WAVES_EVEN
+#define MLA_ATTEND_SCORE_WAVES_EVEN 0
+#endif
+
+// One workgroup = 256 rows x a contiguous range of (row-block, key-tile)
+// units; each row-block segment leaves a partial softmax state (m, l, L) in
+// its slot: score wavefronts write (m, l), value wavefronts write L.
+template <int DC>
+__global__ __launch_bounds__(kWaves * 64, 1)
+void attend_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstride, int n_k,
+                        const u16* __restrict__ qt, int rows_pad_b, int rb_per_b,
+                        float* __restrict__ part_L, float* __restrict__ part_ml,
+                        int T, int64_t U, int G, float headroom) {
+  using L = AttendTile<DC>;
+  __shared__ __attribute__((aligned(1024))) char kbuf0[L::TILEB];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[L::TILEB];
+  __shared__ __attribute__((aligned(1024))) char kbuf2[L::TILEB];
+  __shared__ __attribute__((aligned(1024))) char pbuf0[L::PBUF];
+  __shared__ __attribute__((aligned(1024))) char pbuf1[L::PBUF];
+
+  SweepCtx c;
+  c.n_k = n_k;
+  c.lane = threadIdx.x & 63;
+  c.half = c.lane >> 5;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#if MLA_ATTEND_SCORE_WAVES_EVEN
+  const bool scorer = (c.wave & 1) == 0;
+  c.group = c.wave >> 1;
+#else
+  const bool scorer = c.wave < kGroups;
+  c.group = c.wave & (kGroups - 1);
+#endif
+  c.lane_chunk = lane_copy_chunk<DC>(c.lane, c.lane_row);
+  c.s_off = (c.lane & 31) * L::ROWB + c.half * 16;
+  const int g = c.lane >> 4, j = c.lane & 15;
+  c.v_off = ((g >> 1) * 4 + (j >> 2)) * L::ROWB + (16 * (g & 1) + 4 * (j & 3)) * 2;
+
+  const int64_t w = blockIdx.x;
+  SegmentIter it;
+  it.u = unit_begin(w, U, G);
+  it.u_end = unit_begin(w + 1, U, G);
+  it.T = T;
+  it.rb_per_b = rb_per_b;
+  if (scorer)
+    score_role<DC>(c, it, cache, cache_bstride, qt, rows_pad_b, part_ml, w, headroom, kbuf0, kbuf1, kbuf2, pbuf0,
+                   pbuf1);
+  else
+    value_role<DC>(c, it, cache, cache_bstride, part_L, w, kbuf0, kbuf1, kbuf2, pbuf0, pbuf1);
 }
 
 // fp32 variant: 8 threads per row, 32 rows per workgroup, one workgroup
@@ -424,11 +498,6 @@ void attend_f32_kernel(const float* __restrict__ cache, int64_t cache_bstride, i
   for (int j = 0; j < LJ; ++j) Ld[sub + 8 * j] = lacc[j] * inv;
 }
 
-#ifndef MLA_ATTEND_QB
-#define MLA_ATTEND_QB 1
-#endif
-constexpr int kAttendQB = MLA_ATTEND_QB;
-
 hipError_t launch_attend_bf16(const Plan& p, const AttendArgs& a, hipStream_t s) {
   char* ws = (char*)a.workspace;
   const u16* cache = (const u16*)a.cache;
@@ -437,10 +506,10 @@ hipError_t launch_attend_bf16(const Plan& p, const AttendArgs& a, hipStream_t s)
   float* ml = (float*)(ws + p.off_ml);
   const dim3 grid(p.G);
   switch (p.d_c) {
-    case 64: attend_bf16_kernel<64, kAttendQB><<<grid, dim3(512 / kAttendQB), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
-    case 128: attend_bf16_kernel<128, kAttendQB><<<grid, dim3(512 / kAttendQB), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
-    case 192: attend_bf16_kernel<192, kAttendQB><<<grid, dim3(512 / kAttendQB), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
-    case 256: attend_bf16_kernel<256, kAttendQB><<<grid, dim3(512 / kAttendQB), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
+    case 64: attend_bf16_kernel<64><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
+    case 128: attend_bf16_kernel<128><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
+    case 192: attend_bf16_kernel<192><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
+    case 256: attend_bf16_kernel<256><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -17,8 +17,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Rows of (batch, head, query) handled by one attention workgroup.
 constexpr int kRowsPerBlock = 256;
-// Keys per latent tile staged in LDS.
-constexpr int kKeyTile = 128;
+// Keys per latent tile staged in LDS: three key buffers and two P buffers
+// (16 KB per 32 keys) must fit the 160 KB of LDS.
+__host__ __device__ constexpr int key_tile(int d_c) { return d_c <= 192 ? 64 : 32; }
 // Compute units the work partition is sized for (MI355X).
 constexpr int kPartitionCUs = 256;
 // log2(e): softmax runs in base 2 with this folded into the query scale.
@@ -69,7 +70,7 @@ inline Plan make_plan(int B, int H, int n_q, int n_k, int d_c, int d_r, bool f32
   p.rb_per_b = (p.rows_b + kRowsPerBlock - 1) / kRowsPerBlock;
   p.rows_pad_b = p.rb_per_b * kRowsPerBlock;
   p.nrb = B * p.rb_per_b;
-  p.T = (n_k + kKeyTile - 1) / kKeyTile;
+  p.T = (n_k + key_tile(d_c) - 1) / key_tile(d_c);
   p.U = (int64_t)p.nrb * p.T;
   p.elem = f32 ? 4 : 2;
   int64_t G = p.nrb;
