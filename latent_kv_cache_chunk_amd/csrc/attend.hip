@@ -509,7 +509,7 @@ hipError_t launch_attend_bf16(const Plan& p, const AttendArgs& a, hipStream_t s)
     case 64: attend_bf16_kernel<64><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
     case 128: attend_bf16_kernel<128><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
     case 192: attend_bf16_kernel<192><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
-    case 256: attend_bf16_kernel<256><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
+    case 256: return launch_attend_wide_bf16(p, a, s);   // value accumulators would not fit the role split
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

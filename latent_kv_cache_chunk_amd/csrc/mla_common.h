@@ -17,9 +17,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Rows of (batch, head, query) handled by one attention workgroup.
 constexpr int kRowsPerBlock = 256;
-// Keys per latent tile staged in LDS: three key buffers and two P buffers
-// (16 KB per 32 keys) must fit the 160 KB of LDS.
-__host__ __device__ constexpr int key_tile(int d_c) { return d_c <= 192 ? 64 : 32; }
+// Keys per latent tile staged in LDS.  d_c <= 192 (attend.hip): three key
+// buffers and two P buffers (16 KB per 32 keys) fit the 160 KB of LDS with
+// 64-key tiles.  d_c = 256 (attend_wide.hip): two 128-key buffers.
+__host__ __device__ constexpr int key_tile(int d_c) { return d_c <= 192 ? 64 : 128; }
 // Compute units the work partition is sized for (MI355X).
 constexpr int kPartitionCUs = 256;
 // log2(e): softmax runs in base 2 with this folded into the query scale.

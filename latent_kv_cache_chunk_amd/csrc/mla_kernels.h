@@ -44,6 +44,7 @@ hipError_t launch_append_f32(const AppendArgs& a, hipStream_t s);
 hipError_t launch_absorb_bf16(const Plan& p, const AbsorbArgs& a, hipStream_t s);
 hipError_t launch_absorb_f32(const Plan& p, const AbsorbArgs& a, hipStream_t s);
 hipError_t launch_attend_bf16(const Plan& p, const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_wide_bf16(const Plan& p, const AttendArgs& a, hipStream_t s);   // d_c = 256
 hipError_t launch_attend_f32(const Plan& p, const AttendArgs& a, hipStream_t s);
 hipError_t launch_upproj_bf16(const Plan& p, const UpprojArgs& a, hipStream_t s);
 hipError_t launch_upproj_f32(const Plan& p, const UpprojArgs& a, hipStream_t s);
