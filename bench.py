@@ -75,14 +75,20 @@ def cpu_baseline(wl, inputs, n_heads: int) -> dict:
     w_uk = inputs["w_uk"].cpu().double().numpy()
     w_uv = inputs["w_uv"].cpu().double().numpy()
     cache = inputs["cache"][:, :wl.n_k].cpu().double().numpy()
+    chunks = {}
+    kv = np.full(len(rows), wl.n_k, np.int64)
+    if wl.causal:
+        q_start, c = wl.causal
+        chunks = dict(q_chunk=(q_start + np.arange(wl.n_q)) // c, k_chunk=np.arange(wl.n_k) // c)
+        kv = np.minimum(wl.n_k, ((q_start + rows[:, 1]) // c + 1) * c)
     t0 = time.perf_counter()
     oracle.chunk_attend_rows(rows, args[0], args[1], q_pos, w_uk, w_uv, cache, wl.n_k, wl.scale,
-                             split=wl.rope_split, theta=wl.theta)
+                             split=wl.rope_split, theta=wl.theta, **chunks)
     dt = time.perf_counter() - t0
-    flops = len(rows) * (wl.n_k * (4 * wl.d_c + 2 * wl.d_r) + 4 * wl.head_dim * wl.d_c)
+    flops = float(kv.sum()) * (4 * wl.d_c + 2 * wl.d_r) + len(rows) * 4 * wl.head_dim * wl.d_c
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(rows)} rows (all {wl.n_q} queries of heads 0..{min(n_heads, wl.n_heads) - 1}, "
-                      f"batch 0) against all {wl.n_k} keys, fp64 "
+                      f"batch 0) against their visible keys (of {wl.n_k}), fp64 "
                       f"non-absorbed numpy oracle incl. per-head K/V reconstruction; {dt:.1f} s wall; "
                       f"rate = absorbed algorithmic flops of the sample / wall time"}
 
@@ -130,7 +136,7 @@ def main(argv=None) -> int:
         mla.query_absorb(dims, t["q"], t["q_r"], t["q_pos"], t["w_uk"], wl.scale, wl.n_k, ws)
         if ev is not None:
             ev[2].record()
-        mla.latent_attend(dims, cache, wl.n_q, wl.n_k, ws)
+        mla.latent_attend(dims, cache, wl.n_q, wl.n_k, ws, causal=wl.causal)
         if ev is not None:
             ev[3].record()
         mla.value_upproj(dims, t["w_uv"], out, wl.n_q, wl.n_k, ws)
@@ -188,7 +194,8 @@ def main(argv=None) -> int:
         "data": "synthetic (seeded Gaussian inputs of the workload's shape)",
         "config": {"workload": wl.name, "batch": wl.batch, "n_q": wl.n_q, "n_k": wl.n_k,
                    "heads": wl.n_heads, "head_dim": wl.head_dim, "d_c": wl.d_c, "d_r": wl.d_r,
-                   "rope_split": list(wl.rope_split), "d_model": wl.d_model},
+                   "rope_split": list(wl.rope_split), "d_model": wl.d_model,
+                   "chunk_tokens": wl.chunk_tokens or wl.n_q},
         "frac_bf16_peak": round(value / BF16_PEAK_TFLOPS, 4),
         "breakdown_ms": {"append": round(append_ms, 4), "absorb": round(absorb_ms, 4),
                          "attend": round(attend_ms, 4), "attend_median": round(attend_ms_median, 4),
@@ -198,8 +205,9 @@ def main(argv=None) -> int:
                      "achieved": round(attend_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attend_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "flop_per_launch": core_flops,
-                     "per_unit": f"{4 * wl.d_c + 2 * wl.d_r} flop per (row, key); "
-                                 f"{wl.batch * wl.n_q * wl.n_heads} rows x {wl.n_k} keys per launch"},
+                     "per_unit": f"{4 * wl.d_c + 2 * wl.d_r} flop per visible (row, key); "
+                                 f"{wl.batch * wl.n_heads * wl.visible_keys()} visible pairs per launch "
+                                 f"({wl.batch * wl.n_q * wl.n_heads} rows, {wl.n_k} keys)"},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -136,6 +136,29 @@ int32_t mla_chunk_attend(const mla_dims* dims, int32_t in_dtype, int32_t out_dty
                          float softmax_scale, void* out,
                          void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Chunk-causal visibility for a call whose queries span several chunks (the
+ * training / teacher-forcing form; VideoMLA atlas.scime.ai summary, first
+ * paragraph: causal across chunks, bidirectional inside a chunk).  Query i
+ * of the call is token q_start + i of the key sequence; with chunk length C
+ * it sees keys [0, min(n_k, (floor((q_start + i) / C) + 1) * C)).
+ * Requires C >= 1, q_start >= 0 and q_start + n_q <= n_k.  Tiles that no
+ * query of a 256-row block can see are skipped. */
+typedef struct mla_causal {
+  int32_t q_start;
+  int32_t chunk_len;
+} mla_causal;
+
+/* mla_chunk_attend with chunk-causal visibility (see mla_causal; `causal`
+ * is a host pointer read during the call).  When n_k is a multiple of n_q,
+ * q_start = n_k - n_q and chunk_len = n_q let every query see all n_k keys,
+ * as mla_chunk_attend does. */
+int32_t mla_chunk_attend_causal(const mla_dims* dims, int32_t in_dtype, int32_t out_dtype,
+                                const void* q, const void* q_r, const int32_t* q_pos, int32_t n_q,
+                                const void* w_uk, const void* w_uv,
+                                const void* cache, int32_t cache_capacity, int32_t n_k,
+                                const mla_causal* causal, float softmax_scale, void* out,
+                                void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Step 1 of mla_chunk_attend: writes the absorbed, pre-scaled queries q~
  * (the content part W_UK[h]^T q_h and the rotated positional part, both
  * multiplied by softmax_scale*log2(e), rounded once to the dtype) into the
@@ -151,6 +174,12 @@ int32_t mla_query_absorb(const mla_dims* dims, int32_t dtype,
 int32_t mla_latent_attend(const mla_dims* dims, int32_t dtype,
                           const void* cache, int32_t cache_capacity, int32_t n_q, int32_t n_k,
                           void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Step 2 with chunk-causal visibility (see mla_causal). */
+int32_t mla_latent_attend_causal(const mla_dims* dims, int32_t dtype,
+                                 const void* cache, int32_t cache_capacity, int32_t n_q, int32_t n_k,
+                                 const mla_causal* causal,
+                                 void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Step 3: merges the partial softmax states of each row into L (fp32) and
  * writes out = W_UV[h] L in out_dtype.  Requires steps 1 and 2. */

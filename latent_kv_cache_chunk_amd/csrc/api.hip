@@ -114,13 +114,35 @@ int32_t do_absorb(const mla_dims* d, int32_t dtype, const mla::Plan& p, const vo
   return finish(e, s, "mla_query_absorb");
 }
 
+// Chunk-causal limits of a call (nullptr: every query sees all n_k keys).
+int32_t check_causal(const mla_causal* c, int32_t n_q, int32_t n_k) {
+  if (c == nullptr) return fail(MLA_ERR_INVALID_ARG, "causal is null");
+  if (c->chunk_len < 1) return fail(MLA_ERR_INVALID_ARG, "causal.chunk_len must be >= 1 (got %d)", c->chunk_len);
+  if (c->q_start < 0 || (int64_t)c->q_start + n_q > n_k)
+    return fail(MLA_ERR_INVALID_ARG, "causal.q_start %d + n_q %d must lie within n_k %d", c->q_start, n_q, n_k);
+  if ((int64_t)n_k + c->chunk_len > (int64_t)INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "n_k + chunk_len too large");
+  return MLA_OK;
+}
+
+mla::Visibility visibility(const mla::Plan& p, const mla_causal* causal) {
+  return mla::Visibility{p.n_q, p.rows_b, causal ? causal->q_start : 0, causal ? causal->chunk_len : 0};
+}
+
+// The plan of a chunk-causal call: per-row-block units (same workspace size).
+mla::Plan causal_plan(const mla_dims* d, int32_t dtype, const mla::Plan& p, const mla_causal* causal) {
+  if (causal == nullptr) return p;
+  const mla::Visibility vis = visibility(p, causal);
+  return mla::make_plan(d->batch, d->n_heads, p.n_q, p.n_k, d->d_c, d->d_r, dtype == MLA_F32, &vis);
+}
+
 int32_t do_attend(const mla_dims* d, int32_t dtype, const mla::Plan& p, const void* cache, int32_t cap,
-                  void* ws, hipStream_t s) {
+                  const mla_causal* causal, void* ws, hipStream_t s) {
   mla::AttendArgs a{};
   a.cache = cache;
   a.cache_bstride = (int64_t)cap * (d->d_c + d->d_r);
   a.workspace = ws;
   a.headroom = attend_headroom();
+  a.vis = visibility(p, causal);
   hipError_t e = dtype == MLA_BF16 ? mla::launch_attend_bf16(p, a, s) : mla::launch_attend_f32(p, a, s);
   return finish(e, s, "mla_latent_attend");
 }
@@ -133,6 +155,50 @@ int32_t do_upproj(int32_t dtype, int32_t out_dtype, const mla::Plan& p, const vo
   return finish(e, s, "mla_value_upproj");
 }
 
+}  // namespace
+
+namespace {
+
+int32_t latent_attend_impl(const mla_dims* dims, int32_t dtype, const void* cache, int32_t cache_capacity,
+                           int32_t n_q, int32_t n_k, const mla_causal* causal, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+  mla::Plan p;
+  int32_t st = check_attend_sizes(dims, dtype, n_q, n_k, &p);
+  if (st) return st;
+  if ((st = check_ptr(cache, "cache"))) return st;
+  if (n_k > cache_capacity) return fail(MLA_ERR_INVALID_ARG, "n_k (%d) exceeds cache_capacity (%d)", n_k, cache_capacity);
+  if (causal && (st = check_causal(causal, n_q, n_k))) return st;
+  if ((st = check_workspace(p, workspace, workspace_bytes))) return st;
+  return do_attend(dims, dtype, causal_plan(dims, dtype, p, causal), cache, cache_capacity, causal, workspace,
+                   (hipStream_t)stream);
+}
+
+int32_t chunk_attend_impl(const mla_dims* dims, int32_t in_dtype, int32_t out_dtype, const void* q,
+                          const void* q_r, const int32_t* q_pos, int32_t n_q, const void* w_uk, const void* w_uv,
+                          const void* cache, int32_t cache_capacity, int32_t n_k, const mla_causal* causal,
+                          float softmax_scale, void* out, void* workspace, int64_t workspace_bytes, void* stream) {
+  mla::Plan p;
+  int32_t st = check_attend_sizes(dims, in_dtype, n_q, n_k, &p);
+  if (st) return st;
+  if ((st = check_dtype(out_dtype, "out_dtype"))) return st;
+  if ((st = check_ptr(q, "q"))) return st;
+  if ((st = check_ptr(q_r, "q_r"))) return st;
+  if ((st = check_ptr(q_pos, "q_pos", 4))) return st;
+  if ((st = check_ptr(w_uk, "w_uk"))) return st;
+  if ((st = check_ptr(w_uv, "w_uv"))) return st;
+  if ((st = check_ptr(cache, "cache"))) return st;
+  if ((st = check_ptr(out, "out"))) return st;
+  if (n_k > cache_capacity) return fail(MLA_ERR_INVALID_ARG, "n_k (%d) exceeds cache_capacity (%d)", n_k, cache_capacity);
+  if (causal && (st = check_causal(causal, n_q, n_k))) return st;
+  if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if ((st = check_workspace(p, workspace, workspace_bytes))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = do_absorb(dims, in_dtype, p, q, q_r, q_pos, w_uk, softmax_scale, workspace, s))) return st;
+  if ((st = do_attend(dims, in_dtype, causal_plan(dims, in_dtype, p, causal), cache, cache_capacity, causal,
+                      workspace, s)))
+    return st;
+  return do_upproj(in_dtype, out_dtype, p, w_uv, out, workspace, s);
+}
 }  // namespace
 
 extern "C" {
@@ -189,15 +255,19 @@ int32_t mla_query_absorb(const mla_dims* dims, int32_t dtype, const void* q, con
   return do_absorb(dims, dtype, p, q, q_r, q_pos, w_uk, softmax_scale, workspace, (hipStream_t)stream);
 }
 
+
 int32_t mla_latent_attend(const mla_dims* dims, int32_t dtype, const void* cache, int32_t cache_capacity,
                           int32_t n_q, int32_t n_k, void* workspace, int64_t workspace_bytes, void* stream) {
-  mla::Plan p;
-  int32_t st = check_attend_sizes(dims, dtype, n_q, n_k, &p);
-  if (st) return st;
-  if ((st = check_ptr(cache, "cache"))) return st;
-  if (n_k > cache_capacity) return fail(MLA_ERR_INVALID_ARG, "n_k (%d) exceeds cache_capacity (%d)", n_k, cache_capacity);
-  if ((st = check_workspace(p, workspace, workspace_bytes))) return st;
-  return do_attend(dims, dtype, p, cache, cache_capacity, workspace, (hipStream_t)stream);
+  return latent_attend_impl(dims, dtype, cache, cache_capacity, n_q, n_k, nullptr, workspace, workspace_bytes,
+                            stream);
+}
+
+int32_t mla_latent_attend_causal(const mla_dims* dims, int32_t dtype, const void* cache, int32_t cache_capacity,
+                                 int32_t n_q, int32_t n_k, const mla_causal* causal, void* workspace,
+                                 int64_t workspace_bytes, void* stream) {
+  if (causal == nullptr) return fail(MLA_ERR_INVALID_ARG, "causal is null");
+  return latent_attend_impl(dims, dtype, cache, cache_capacity, n_q, n_k, causal, workspace, workspace_bytes,
+                            stream);
 }
 
 int32_t mla_value_upproj(const mla_dims* dims, int32_t dtype, int32_t out_dtype, int32_t n_q, int32_t n_k,
@@ -216,24 +286,18 @@ int32_t mla_chunk_attend(const mla_dims* dims, int32_t in_dtype, int32_t out_dty
                          const int32_t* q_pos, int32_t n_q, const void* w_uk, const void* w_uv, const void* cache,
                          int32_t cache_capacity, int32_t n_k, float softmax_scale, void* out, void* workspace,
                          int64_t workspace_bytes, void* stream) {
-  mla::Plan p;
-  int32_t st = check_attend_sizes(dims, in_dtype, n_q, n_k, &p);
-  if (st) return st;
-  if ((st = check_dtype(out_dtype, "out_dtype"))) return st;
-  if ((st = check_ptr(q, "q"))) return st;
-  if ((st = check_ptr(q_r, "q_r"))) return st;
-  if ((st = check_ptr(q_pos, "q_pos", 4))) return st;
-  if ((st = check_ptr(w_uk, "w_uk"))) return st;
-  if ((st = check_ptr(w_uv, "w_uv"))) return st;
-  if ((st = check_ptr(cache, "cache"))) return st;
-  if ((st = check_ptr(out, "out"))) return st;
-  if (n_k > cache_capacity) return fail(MLA_ERR_INVALID_ARG, "n_k (%d) exceeds cache_capacity (%d)", n_k, cache_capacity);
-  if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
-  if ((st = check_workspace(p, workspace, workspace_bytes))) return st;
-  hipStream_t s = (hipStream_t)stream;
-  if ((st = do_absorb(dims, in_dtype, p, q, q_r, q_pos, w_uk, softmax_scale, workspace, s))) return st;
-  if ((st = do_attend(dims, in_dtype, p, cache, cache_capacity, workspace, s))) return st;
-  return do_upproj(in_dtype, out_dtype, p, w_uv, out, workspace, s);
+  return chunk_attend_impl(dims, in_dtype, out_dtype, q, q_r, q_pos, n_q, w_uk, w_uv, cache, cache_capacity, n_k,
+                           nullptr, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+int32_t mla_chunk_attend_causal(const mla_dims* dims, int32_t in_dtype, int32_t out_dtype, const void* q,
+                                const void* q_r, const int32_t* q_pos, int32_t n_q, const void* w_uk,
+                                const void* w_uv, const void* cache, int32_t cache_capacity, int32_t n_k,
+                                const mla_causal* causal, float softmax_scale, void* out, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
+  if (causal == nullptr) return fail(MLA_ERR_INVALID_ARG, "causal is null");
+  return chunk_attend_impl(dims, in_dtype, out_dtype, q, q_r, q_pos, n_q, w_uk, w_uv, cache, cache_capacity, n_k,
+                           causal, softmax_scale, out, workspace, workspace_bytes, stream);
 }
 
 const char* mla_status_string(int32_t status) {

@@ -96,6 +96,9 @@ __device__ inline int lane_copy_chunk(int lane, int& lane_row) {
 struct SweepCtx {
   const char* gbase;   // cache rows of this sample
   int n_k;
+  bool causal;         // keys limited per row (chunk-causal visibility)
+  int kv[2];           // score lanes: visible keys of the lane's row in each half
+  int kv_min;          // score wavefronts: smallest kv of the wavefront
   int wave, lane, half, group;
   int lane_chunk, lane_row;
   int s_off;           // b128 score operand offset inside a block
@@ -183,7 +186,13 @@ __device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile,
       s[0] = mfma_32x32x16(cur, st.qf[0][ks], s[0]);
       s[1] = mfma_32x32x16(cur, st.qf[1][ks], s[1]);
     }
-    if (left - kb * 32 < 32) {
+    const int key0 = t * L::BN + kb * 32;
+    if (c.causal) {
+      if (key0 + 32 > c.kv_min) {   // some row of the wavefront ends inside this block
+        mask_block(s[0], c.kv[0] - key0, c.half);
+        mask_block(s[1], c.kv[1] - key0, c.half);
+      }
+    } else if (left - kb * 32 < 32) {
       mask_block(s[0], left - kb * 32, c.half);
       mask_block(s[1], left - kb * 32, c.half);
     }
@@ -194,7 +203,8 @@ __device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile,
         continue;
       }
       if (P == Pass::kSingle && first_tile && kb == 0) st.m_ref[qb] = block_max(s[qb]);
-      const float m = st.m_ref[qb];
+      // a row with no visible key in this segment keeps m = -inf and p = 0
+      const float m = st.m_ref[qb] == -INFINITY ? 0.f : st.m_ref[qb];
       float p[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(s[qb][v] - m);
@@ -289,18 +299,22 @@ __device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* k2, c
   }
 }
 
-// Segments of workgroup w: contiguous (row-block, key-tile) unit ranges, at
-// most two row blocks.
+// Segments of workgroup w: its contiguous unit range, cut at row-block
+// boundaries (see Plan).
 struct SegmentIter {
   int64_t u, u_end;
   int T, rb_per_b;
+  const int64_t* units;   // first unit of each row block (chunk-causal), or nullptr
+  int64_t nrb;
   int64_t rb;
   int t0, t1, b, rbl;
   __device__ bool next() {
     if (u >= u_end) return false;
-    rb = u / T;
-    t0 = (int)(u - rb * T);
-    t1 = (int)min<int64_t>((int64_t)T, (int64_t)t0 + (u_end - u));
+    rb = rb_of_unit(units, T, nrb, u);
+    const int64_t first = rb_first_unit(units, T, rb);
+    const int64_t n_units = (units ? units[rb + 1] : first + T) - first;
+    t0 = (int)(u - first);
+    t1 = (int)min<int64_t>(n_units, (int64_t)t0 + (u_end - u));
     b = (int)(rb / rb_per_b);
     rbl = (int)(rb - (int64_t)b * rb_per_b);
     u += (t1 - t0);
@@ -308,16 +322,32 @@ struct SegmentIter {
   }
 };
 
+// End of the segment's tiles that some row of the row block can see (t1 when
+// every key is visible); a segment that ends at or before t0 is empty.
+template <int DC>
+__device__ __forceinline__ int visible_end(const SegmentIter& it, const Visibility& vis, int n_k) {
+  constexpr int BN = AttendTile<DC>::BN;
+  const int kv = vis.kv_max_of_block(it.rbl * kRowsPerBlock, n_k);
+  return min(it.t1, (kv + BN - 1) / BN);
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+
 template <int DC>
 __device__ __forceinline__ void score_role(SweepCtx& c, SegmentIter it, const u16* __restrict__ cache,
                                            int64_t cache_bstride, const u16* __restrict__ qt, int rows_pad_b,
-                                           float* __restrict__ part_ml, int64_t w, float headroom, char* k0,
-                                           char* k1, char* k2, char* pb0, char* pb1) {
+                                           float* __restrict__ part_ml, int64_t w, float headroom,
+                                           const Visibility& vis, char* k0, char* k1, char* k2, char* pb0,
+                                           char* pb1) {
   using L = AttendTile<DC>;
   ScoreState<DC> st;
-  bool first_seg = true;
   while (it.next()) {
     c.gbase = reinterpret_cast<const char*>(cache + (int64_t)it.b * cache_bstride);
+    const int te = visible_end<DC>(it, vis, c.n_k);
     const int64_t row0 = (int64_t)it.b * rows_pad_b + (int64_t)it.rbl * kRowsPerBlock + c.group * kGroupRows;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -325,19 +355,21 @@ __device__ __forceinline__ void score_role(SweepCtx& c, SegmentIter it, const u1
 #pragma unroll
       for (int ks = 0; ks < L::KS; ++ks) st.qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
       st.l_run[qb] = 0.f;
+      st.m_ref[qb] = -INFINITY;
+      c.kv[qb] = vis.kv_of_row(it.rbl * kRowsPerBlock + c.group * kGroupRows + qb * 32 + (c.lane & 31), c.n_k);
     }
-    sweep<DC, Pass::kSingle, true>(st, k0, k1, k2, pb0, pb1, it.t0, it.t1, c);
+    c.kv_min = wave_min(min(c.kv[0], c.kv[1]));
+    if (te > it.t0) sweep<DC, Pass::kSingle, true>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
     const float lim = __builtin_amdgcn_exp2f(headroom);
     const bool over = !(st.l_run[0] <= lim) || !(st.l_run[1] <= lim);
     if (__syncthreads_or(over)) {
       // A running sum rose past 2^headroom: exact two-pass evaluation.
       st.m_ref[0] = st.m_ref[1] = -INFINITY;
-      sweep<DC, Pass::kMax, true>(st, k0, k1, k2, pb0, pb1, it.t0, it.t1, c);
+      sweep<DC, Pass::kMax, true>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
       st.l_run[0] = st.l_run[1] = 0.f;
-      sweep<DC, Pass::kAccum, true>(st, k0, k1, k2, pb0, pb1, it.t0, it.t1, c);
+      sweep<DC, Pass::kAccum, true>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
     }
-    const int64_t slot = 2 * w + (first_seg ? 0 : 1);
-    first_seg = false;
+    const int64_t slot = seg_slot(w, it.rb);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float l_tot = st.l_run[qb] + __shfl_xor(st.l_run[qb], 32);
@@ -352,18 +384,19 @@ __device__ __forceinline__ void score_role(SweepCtx& c, SegmentIter it, const u1
 
 template <int DC>
 __device__ __forceinline__ void value_role(SweepCtx& c, SegmentIter it, const u16* __restrict__ cache,
-                                           int64_t cache_bstride, float* __restrict__ part_L, int64_t w, char* k0,
-                                           char* k1, char* k2, char* pb0, char* pb1) {
+                                           int64_t cache_bstride, float* __restrict__ part_L, int64_t w,
+                                           const Visibility& vis, char* k0, char* k1, char* k2, char* pb0,
+                                           char* pb1) {
   using L = AttendTile<DC>;
   ValueState<DC> st;
-  bool first_seg = true;
   while (it.next()) {
     c.gbase = reinterpret_cast<const char*>(cache + (int64_t)it.b * cache_bstride);
+    const int te = visible_end<DC>(it, vis, c.n_k);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int cb = 0; cb < L::CB; ++cb) st.oacc[qb][cb] = f32x16{};
-    sweep<DC, Pass::kSingle, false>(st, k0, k1, k2, pb0, pb1, it.t0, it.t1, c);
+    if (te > it.t0) sweep<DC, Pass::kSingle, false>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -372,15 +405,14 @@ __device__ __forceinline__ void value_role(SweepCtx& c, SegmentIter it, const u1
 #pragma unroll
         for (int v = 0; v < 16; ++v) bad |= !(fabsf(st.oacc[qb][cb][v]) <= 3.0e38f);
     if (__syncthreads_or(bad)) {
-      sweep<DC, Pass::kMax, false>(st, k0, k1, k2, pb0, pb1, it.t0, it.t1, c);
+      sweep<DC, Pass::kMax, false>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int cb = 0; cb < L::CB; ++cb) st.oacc[qb][cb] = f32x16{};
-      sweep<DC, Pass::kAccum, false>(st, k0, k1, k2, pb0, pb1, it.t0, it.t1, c);
+      sweep<DC, Pass::kAccum, false>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
     }
-    const int64_t slot = 2 * w + (first_seg ? 0 : 1);
-    first_seg = false;
+    const int64_t slot = seg_slot(w, it.rb);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int rl = c.group * kGroupRows + qb * 32 + (c.lane & 31);
@@ -397,10 +429,6 @@ __device__ __forceinline__ void value_role(SweepCtx& c, SegmentIter it, const u1
   }
 }
 
-#ifndef MLA_ATTEND_SCORE_WAVES_EVEN
-#define MLA_ATTEND_SCORE_WAVES_EVEN 0
-#endif
-
 // One workgroup = 256 rows x a contiguous range of (row-block, key-tile)
 // units; each row-block segment leaves a partial softmax state (m, l, L) in
 // its slot: score wavefronts write (m, l), value wavefronts write L.
@@ -409,7 +437,8 @@ __global__ __launch_bounds__(kWaves * 64, 1)
 void attend_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstride, int n_k,
                         const u16* __restrict__ qt, int rows_pad_b, int rb_per_b,
                         float* __restrict__ part_L, float* __restrict__ part_ml,
-                        int T, int64_t U, int G, float headroom) {
+                        int T, int64_t U, int G, float headroom, Visibility vis,
+                        const int64_t* __restrict__ units, int64_t nrb, PartitionHeader* __restrict__ hdr) {
   using L = AttendTile<DC>;
   __shared__ __attribute__((aligned(1024))) char kbuf0[L::TILEB];
   __shared__ __attribute__((aligned(1024))) char kbuf1[L::TILEB];
@@ -419,32 +448,35 @@ void attend_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstride, in
 
   SweepCtx c;
   c.n_k = n_k;
+  c.causal = vis.chunk_len != 0;
+  c.kv[0] = c.kv[1] = c.kv_min = n_k;
   c.lane = threadIdx.x & 63;
   c.half = c.lane >> 5;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#if MLA_ATTEND_SCORE_WAVES_EVEN
-  const bool scorer = (c.wave & 1) == 0;
-  c.group = c.wave >> 1;
-#else
-  const bool scorer = c.wave < kGroups;
+  const bool scorer = c.wave < kGroups;   // wavefronts w and w + 4 share a SIMD
   c.group = c.wave & (kGroups - 1);
-#endif
   c.lane_chunk = lane_copy_chunk<DC>(c.lane, c.lane_row);
   c.s_off = (c.lane & 31) * L::ROWB + c.half * 16;
   const int g = c.lane >> 4, j = c.lane & 15;
   c.v_off = ((g >> 1) * 4 + (j >> 2)) * L::ROWB + (16 * (g & 1) + 4 * (j & 3)) * 2;
 
-  const int64_t w = blockIdx.x;
+  // Workgroups are dispatched last unit range first: with chunk-causal
+  // visibility the last row blocks see the most keys, and starting the
+  // longest ranges first keeps the tail of the launch short.
+  const int64_t w = (int64_t)G - 1 - blockIdx.x;
   SegmentIter it;
   it.u = unit_begin(w, U, G);
   it.u_end = unit_begin(w + 1, U, G);
   it.T = T;
   it.rb_per_b = rb_per_b;
+  it.units = units;
+  it.nrb = nrb;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *hdr = PartitionHeader{U, G, units != nullptr ? 1 : 0};
   if (scorer)
-    score_role<DC>(c, it, cache, cache_bstride, qt, rows_pad_b, part_ml, w, headroom, kbuf0, kbuf1, kbuf2, pbuf0,
-                   pbuf1);
+    score_role<DC>(c, it, cache, cache_bstride, qt, rows_pad_b, part_ml, w, headroom, vis, kbuf0, kbuf1, kbuf2,
+                   pbuf0, pbuf1);
   else
-    value_role<DC>(c, it, cache, cache_bstride, part_L, w, kbuf0, kbuf1, kbuf2, pbuf0, pbuf1);
+    value_role<DC>(c, it, cache, cache_bstride, part_L, w, vis, kbuf0, kbuf1, kbuf2, pbuf0, pbuf1);
 }
 
 // fp32 variant: 8 threads per row, 32 rows per workgroup, one workgroup
@@ -454,7 +486,7 @@ template <int DC>
 __global__ __launch_bounds__(256)
 void attend_f32_kernel(const float* __restrict__ cache, int64_t cache_bstride, int n_k,
                        const float* __restrict__ qt, int rows_pad_b, int rb_per_b,
-                       float* __restrict__ part_L) {
+                       float* __restrict__ part_L, Visibility vis) {
   constexpr int W = DC + 32, BN = 32, QJ = W / 8, LJ = DC / 8;
   __shared__ float sK[BN * W];
   const int tid = threadIdx.x, rloc = tid >> 3, sub = tid & 7;
@@ -469,12 +501,17 @@ void attend_f32_kernel(const float* __restrict__ cache, int64_t cache_bstride, i
   for (int j = 0; j < LJ; ++j) lacc[j] = 0.f;
   float m = -INFINITY, l = 0.f;
   const float* cbase = cache + (int64_t)b * cache_bstride;
-  for (int key0 = 0; key0 < n_k; key0 += BN) {
-    const int nk = min(BN, n_k - key0);
+  // keys [0, kv_row) are visible to this row; the workgroup sweeps to the
+  // largest kv of its 32 rows (key 0 is visible to every row)
+  const int kv_row = vis.kv_of_row(r, n_k);
+  const int kv_wg = vis.kv_max_of_rows(r - rloc, 32, n_k);
+  for (int key0 = 0; key0 < kv_wg; key0 += BN) {
+    const int nk = min(BN, kv_wg - key0);
     __syncthreads();
     for (int e = tid; e < nk * W; e += 256) sK[e] = cbase[(int64_t)key0 * W + e];
     __syncthreads();
-    for (int k = 0; k < nk; ++k) {
+    const int nk_row = min(nk, kv_row - key0);
+    for (int k = 0; k < nk_row; ++k) {
       const float* kr = sK + k * W;
       float d = 0.f;
 #pragma unroll
@@ -498,17 +535,56 @@ void attend_f32_kernel(const float* __restrict__ cache, int64_t cache_bstride, i
   for (int j = 0; j < LJ; ++j) Ld[sub + 8 * j] = lacc[j] * inv;
 }
 
+// units[rb] of a chunk-causal call: exclusive prefix sum over row blocks of
+// the key tiles some row of the block can see (Plan), units[nrb] = U.  One
+// workgroup; each thread sums a contiguous run of row blocks.
+__global__ __launch_bounds__(1024)
+void units_kernel(int64_t* __restrict__ units, int nrb, int rb_per_b, int n_k, int bn, Visibility vis) {
+  __shared__ int64_t part[1024];
+  const int t = threadIdx.x, per = (nrb + 1023) / 1024;
+  const int r0 = min(nrb, t * per), r1 = min(nrb, r0 + per);
+  auto tiles = [&](int rb) { return (int64_t)((vis.kv_max_of_block((rb % rb_per_b) * kRowsPerBlock, n_k) + bn - 1) / bn); };
+  int64_t sum = 0;
+  for (int rb = r0; rb < r1; ++rb) sum += tiles(rb);
+  part[t] = sum;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan of the per-thread sums
+    const int64_t v = t >= o ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int64_t run = part[t] - sum;
+  for (int rb = r0; rb < r1; ++rb) {
+    units[rb] = run;
+    run += tiles(rb);
+  }
+  if (t == 1023) units[nrb] = part[1023];
+}
+
+hipError_t launch_units(const Plan& p, const AttendArgs& a, hipStream_t s) {
+  int64_t* units = (int64_t*)((char*)a.workspace + p.off_units);
+  units_kernel<<<1, 1024, 0, s>>>(units, p.nrb, p.rb_per_b, p.n_k, key_tile(p.d_c), a.vis);
+  return hipGetLastError();
+}
+
 hipError_t launch_attend_bf16(const Plan& p, const AttendArgs& a, hipStream_t s) {
   char* ws = (char*)a.workspace;
+  const int64_t* units = p.causal ? (const int64_t*)(ws + p.off_units) : nullptr;
+  PartitionHeader* hdr = (PartitionHeader*)(ws + p.off_hdr);
+  if (p.causal) {
+    const hipError_t e = launch_units(p, a, s);
+    if (e != hipSuccess) return e;
+  }
   const u16* cache = (const u16*)a.cache;
   const u16* qt = (const u16*)(ws + p.off_qt);
   float* L = (float*)(ws + p.off_L);
   float* ml = (float*)(ws + p.off_ml);
   const dim3 grid(p.G);
   switch (p.d_c) {
-    case 64: attend_bf16_kernel<64><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
-    case 128: attend_bf16_kernel<128><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
-    case 192: attend_bf16_kernel<192><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom); break;
+    case 64: attend_bf16_kernel<64><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom, a.vis, units, p.nrb, hdr); break;
+    case 128: attend_bf16_kernel<128><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom, a.vis, units, p.nrb, hdr); break;
+    case 192: attend_bf16_kernel<192><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom, a.vis, units, p.nrb, hdr); break;
     case 256: return launch_attend_wide_bf16(p, a, s);   // value accumulators would not fit the role split
     default: return hipErrorInvalidValue;
   }
@@ -522,10 +598,10 @@ hipError_t launch_attend_f32(const Plan& p, const AttendArgs& a, hipStream_t s) 
   float* L = (float*)(ws + p.off_L);
   const dim3 grid(p.B * (p.rows_pad_b / 32)), block(256);
   switch (p.d_c) {
-    case 64: attend_f32_kernel<64><<<grid, block, 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L); break;
-    case 128: attend_f32_kernel<128><<<grid, block, 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L); break;
-    case 192: attend_f32_kernel<192><<<grid, block, 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L); break;
-    case 256: attend_f32_kernel<256><<<grid, block, 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L); break;
+    case 64: attend_f32_kernel<64><<<grid, block, 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, a.vis); break;
+    case 128: attend_f32_kernel<128><<<grid, block, 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, a.vis); break;
+    case 192: attend_f32_kernel<192><<<grid, block, 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, a.vis); break;
+    case 256: attend_f32_kernel<256><<<grid, block, 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, a.vis); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

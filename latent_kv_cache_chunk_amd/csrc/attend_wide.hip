@@ -106,6 +106,9 @@ struct WaveState {
   f32x16 oacc[QB][CB];   // O^T accumulators (latent columns x rows)
   float m_ref[QB];       // reference max (base 2), identical in lanes l and l^32
   float l_run[QB];       // this lane's part of the running sum
+  int kv[QB];            // visible keys of the lane's row in each block (chunk-causal)
+  int kv_min;            // smallest kv of the wavefront
+  bool causal;
 };
 
 enum class Pass { kSingle, kMax, kAccum };
@@ -170,7 +173,8 @@ __device__ __forceinline__ void block_softmax(WaveState<DC, QB>& st, f32x16 (&s)
       st.m_ref[qb] = first_block ? mx : st.m_ref[qb];
       over |= mx > st.m_ref[qb] + headroom;
     }
-    const float m = st.m_ref[qb];
+    // a row with no visible key in this segment keeps m = -inf and p = 0
+    const float m = st.m_ref[qb] == -INFINITY ? 0.f : st.m_ref[qb];
     float lsum = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -215,7 +219,7 @@ __device__ __forceinline__ void block_pv(WaveState<DC, QB>& st, const char* bloc
 // One staged tile, block by block (scores, softmax, P.V).  `left` = keys of
 // the tile that exist; blocks past it are skipped, keys past it masked.
 template <int DC, int QB, int NW, Pass P>
-__device__ __forceinline__ void attend_tile(WaveState<DC, QB>& st, const char* tile, int left, int s_off,
+__device__ __forceinline__ void attend_tile(WaveState<DC, QB>& st, const char* tile, int key0, int left, int s_off,
                                             int v_off, int half, bool first_tile, float headroom, bool& over) {
   using L = AttendTile<DC, NW>;
   constexpr int ROWB = L::ROWB;
@@ -226,7 +230,16 @@ __device__ __forceinline__ void attend_tile(WaveState<DC, QB>& st, const char* t
     f32x16 s[QB];
     bf16x8 pb[QB][2];
     block_scores<DC, QB>(st, tile + kb * 32 * ROWB + s_off, s);
-    if (n_valid < 32) {
+    const int bkey = key0 + kb * 32;
+    if (st.causal && bkey + 32 > st.kv_min) {   // some row of the wavefront ends inside this block
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int thr = st.kv[qb] - bkey - half * 4;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if ((v >> 2) * 8 + (v & 3) >= thr) s[qb][v] = -INFINITY;
+      }
+    } else if (n_valid < 32) {
       const int thr = n_valid - half * 4;   // value v is key (v>>2)*8 + (v&3) + 4*half of the block
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -257,12 +270,12 @@ __device__ __forceinline__ bool sweep(WaveState<DC, QB>& st, char* sbuf0, char* 
   for (int t = t0; t < t1; t += 2) {
     // tile t is in sbuf0; tile t+1 goes to sbuf1
     if (t + 1 < t1) issue_tile<DC, NW>(gbase, (t + 1) * BN, n_k, sbuf1, wave, lane_off, lane_row);
-    attend_tile<DC, QB, NW, P>(st, sbuf0, n_k - t * BN, s_off, v_off, half, t == t0, headroom, over);
+    attend_tile<DC, QB, NW, P>(st, sbuf0, t * BN, n_k - t * BN, s_off, v_off, half, t == t0, headroom, over);
     wait_vmcnt0();
     __syncthreads();
     if (t + 1 >= t1) break;
     if (t + 2 < t1) issue_tile<DC, NW>(gbase, (t + 2) * BN, n_k, sbuf0, wave, lane_off, lane_row);
-    attend_tile<DC, QB, NW, P>(st, sbuf1, n_k - (t + 1) * BN, s_off, v_off, half, false, headroom, over);
+    attend_tile<DC, QB, NW, P>(st, sbuf1, (t + 1) * BN, n_k - (t + 1) * BN, s_off, v_off, half, false, headroom, over);
     wait_vmcnt0();
     __syncthreads();
   }
@@ -286,7 +299,8 @@ __global__ __launch_bounds__(512 / QB, 1)
 void attend_wide_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstride, int n_k,
                         const u16* __restrict__ qt, int rows_pad_b, int rb_per_b,
                         float* __restrict__ part_L, float* __restrict__ part_ml,
-                        int T, int64_t U, int G, float headroom) {
+                        int T, int64_t U, int G, float headroom, Visibility vis,
+                        const int64_t* __restrict__ units, int64_t nrb, PartitionHeader* __restrict__ hdr) {
   constexpr int NW = 8 / QB;   // wavefronts per workgroup
   using L = AttendTile<DC, NW>;
   constexpr int W = L::W, KS = WaveState<DC, QB>::KS, CB = WaveState<DC, QB>::CB, ROWB = L::ROWB;
@@ -304,16 +318,22 @@ void attend_wide_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstrid
   const int g = lane >> 4, j = lane & 15;
   const int v_off = ((g >> 1) * 4 + (j >> 2)) * ROWB + (16 * (g & 1) + 4 * (j & 3)) * 2;
 
-  const int64_t w = blockIdx.x;
+  // Workgroups are dispatched last unit range first: with chunk-causal
+  // visibility the last row blocks see the most keys, and starting the
+  // longest ranges first keeps the tail of the launch short.
+  const int64_t w = (int64_t)G - 1 - blockIdx.x;
   int64_t u = unit_begin(w, U, G);
   const int64_t u_end = unit_begin(w + 1, U, G);
-  bool first_seg = true;
   WaveState<DC, QB> st;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *hdr = PartitionHeader{U, G, units != nullptr ? 1 : 0};
 
   while (u < u_end) {
-    const int64_t rb = u / T;
-    const int t0 = (int)(u - rb * T);
-    const int t1 = (int)min<int64_t>((int64_t)T, (int64_t)t0 + (u_end - u));
+    // this segment: the part of the range inside one row block (see Plan)
+    const int64_t rb = rb_of_unit(units, T, nrb, u);
+    const int64_t first = rb_first_unit(units, T, rb);
+    const int64_t n_units = (units ? units[rb + 1] : first + T) - first;
+    const int t0 = (int)(u - first);
+    const int t1 = (int)min<int64_t>(n_units, (int64_t)t0 + (u_end - u));
     const int b = (int)(rb / rb_per_b);
     const int rbl = (int)(rb - (int64_t)b * rb_per_b);
     const char* gbase = reinterpret_cast<const char*>(cache + (int64_t)b * cache_bstride);
@@ -328,24 +348,34 @@ void attend_wide_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstrid
       }
     }
     reset_acc<DC, QB>(st);
+    // tiles past every row's visible keys are skipped (chunk-causal calls)
+    const int te = min(t1, (vis.kv_max_of_block(rbl * kRowsPerBlock, n_k) + L::BN - 1) / L::BN);
+    st.causal = vis.chunk_len != 0;
+    int kvm = n_k;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) st.m_ref[qb] = -INFINITY;
-    if (sweep<DC, QB, NW, Pass::kSingle>(st, sbuf0, sbuf1, gbase, t0, t1, n_k, wave, lane_off, lane_row, s_off,
-                                         v_off, half, headroom)) {
+    for (int qb = 0; qb < QB; ++qb) {
+      st.m_ref[qb] = -INFINITY;
+      st.kv[qb] = vis.kv_of_row(rbl * kRowsPerBlock + wave * 32 * QB + qb * 32 + (lane & 31), n_k);
+      kvm = min(kvm, st.kv[qb]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) kvm = min(kvm, __shfl_xor(kvm, o));
+    st.kv_min = kvm;
+    if (te > t0 && sweep<DC, QB, NW, Pass::kSingle>(st, sbuf0, sbuf1, gbase, t0, te, n_k, wave, lane_off, lane_row,
+                                                    s_off, v_off, half, headroom)) {
       // Some score rose more than the headroom above its first-block max:
       // exact two-pass evaluation of this segment.
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) st.m_ref[qb] = -INFINITY;
-      sweep<DC, QB, NW, Pass::kMax>(st, sbuf0, sbuf1, gbase, t0, t1, n_k, wave, lane_off, lane_row, s_off, v_off,
+      sweep<DC, QB, NW, Pass::kMax>(st, sbuf0, sbuf1, gbase, t0, te, n_k, wave, lane_off, lane_row, s_off, v_off,
                                     half, headroom);
       reset_acc<DC, QB>(st);
-      sweep<DC, QB, NW, Pass::kAccum>(st, sbuf0, sbuf1, gbase, t0, t1, n_k, wave, lane_off, lane_row, s_off,
+      sweep<DC, QB, NW, Pass::kAccum>(st, sbuf0, sbuf1, gbase, t0, te, n_k, wave, lane_off, lane_row, s_off,
                                       v_off, half, headroom);
     }
 
     // ---- write this segment's partial softmax state
-    const int64_t slot = 2 * w + (first_seg ? 0 : 1);
-    first_seg = false;
+    const int64_t slot = seg_slot(w, rb);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float l_tot = st.l_run[qb] + __shfl_xor(st.l_run[qb], 32);
@@ -376,10 +406,12 @@ hipError_t launch_attend_wide_bf16(const Plan& p, const AttendArgs& a, hipStream
   const u16* qt = (const u16*)(ws + p.off_qt);
   float* L = (float*)(ws + p.off_L);
   float* ml = (float*)(ws + p.off_ml);
+  const int64_t* units = p.causal ? (const int64_t*)(ws + p.off_units) : nullptr;
+  PartitionHeader* hdr = (PartitionHeader*)(ws + p.off_hdr);
   if (p.d_c != 256) return hipErrorInvalidValue;
   wide::attend_wide_bf16_kernel<256, 1><<<dim3(p.G), dim3(512), 0, s>>>(cache, a.cache_bstride, p.n_k, qt,
                                                                         p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U,
-                                                                        p.G, a.headroom);
+                                                                        p.G, a.headroom, a.vis, units, p.nrb, hdr);
   return hipGetLastError();
 }
 

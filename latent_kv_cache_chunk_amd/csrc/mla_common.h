@@ -27,15 +27,45 @@ constexpr int kPartitionCUs = 256;
 constexpr double kLog2e = 1.4426950408889634074;
 
 // ---------------------------------------------------------------------------
+// Chunk-causal visibility.  Query i of a call is token q_start + i of the key
+// sequence; with chunk length C it sees keys [0, kv(i)) where
+//   kv(i) = min(n_k, (floor((q_start + i) / C) + 1) * C)
+// (every earlier chunk and its own chunk, bidirectionally).  chunk_len == 0:
+// every query sees all n_k keys.  Rows are r = h * n_q + i per sample; rows
+// past H * n_q are padding and see one key (their output is never read).
+// ---------------------------------------------------------------------------
+struct Visibility {
+  int n_q, rows_b, q_start, chunk_len;
+
+  __host__ __device__ int kv_of_row(int r, int n_k) const {
+    if (chunk_len == 0) return n_k;
+    if (r >= rows_b) return 1;
+    const int i = r % n_q;
+    return min(n_k, ((q_start + i) / chunk_len + 1) * chunk_len);
+  }
+  // Largest kv over rows [r0, r0 + nrows) (kv grows with i inside a head, so
+  // the last row decides unless the range crosses into a new head).
+  __host__ __device__ int kv_max_of_rows(int r0, int nrows, int n_k) const {
+    if (chunk_len == 0) return n_k;
+    const int r1 = min(r0 + nrows, rows_b) - 1;
+    if (r1 < r0) return 1;
+    return (r0 / n_q != r1 / n_q) ? kv_of_row((r0 / n_q) * n_q + n_q - 1, n_k) : kv_of_row(r1, n_k);
+  }
+  __host__ __device__ int kv_max_of_block(int r0, int n_k) const { return kv_max_of_rows(r0, kRowsPerBlock, n_k); }
+};
+
+// ---------------------------------------------------------------------------
 // Work partition of the fused attention kernel.
 //
-// The (row-block, key-tile) space has U = nrb * T units.  G workgroups each
-// take the contiguous unit range [floor(w*U/G), floor((w+1)*U/G)).  With
-// G >= nrb a range is at most T units long, so it touches at most two
-// row-blocks; the first row-block segment of workgroup w is stored in slot
-// 2w and a second one in slot 2w+1.  A row-block whose units all belong to
-// one workgroup still goes through a slot (one segment).  The combine step
-// finds the owners of a row-block's first and last unit arithmetically.
+// Units are (row-block, key-tile) pairs.  Every key tile of a row block is a
+// unit (T per row block) unless the call is chunk-causal: then a row block
+// has only the tiles some of its rows can see, and units[rb] (an exclusive
+// prefix sum, in the workspace) gives the first unit of row block rb.  G
+// workgroups each take the contiguous unit range [floor(w*U/G),
+// floor((w+1)*U/G)) and leave one partial softmax state per row block they
+// touch, in slot w + rb: a workgroup's row blocks are consecutive, so these
+// slots are distinct, and fewer than G + nrb.  The merge step finds the
+// owners of a row block's first and last unit arithmetically.
 // ---------------------------------------------------------------------------
 struct Plan {
   int32_t B, H, n_q, n_k, d_c, width;   // width = d_c + d_r
@@ -44,11 +74,19 @@ struct Plan {
   int32_t rows_pad_b;   // rb_per_b * kRowsPerBlock
   int32_t nrb;          // B * rb_per_b
   int32_t T;            // key tiles
-  int64_t U;            // nrb * T
+  int64_t U;            // units
   int32_t G;            // attention workgroups
+  bool causal;          // per-row-block units (chunk-causal call)
   int32_t elem;         // bytes per element of q~ (2 bf16, 4 f32)
   // byte offsets inside the workspace
-  int64_t off_qt, off_L, off_ml, total;
+  int64_t off_qt, off_L, off_ml, off_units, off_hdr, total;
+};
+
+// The partition the attention kernel used, left in the workspace for the merge.
+struct PartitionHeader {
+  int64_t U;
+  int32_t G;
+  int32_t per_block_units;   // 1: units[] holds each row block's first unit; 0: row block rb starts at rb * T
 };
 
 __host__ __device__ inline int64_t unit_begin(int64_t w, int64_t U, int64_t G) {
@@ -58,20 +96,40 @@ __host__ __device__ inline int64_t unit_begin(int64_t w, int64_t U, int64_t G) {
 __host__ __device__ inline int64_t unit_owner(int64_t u, int64_t U, int64_t G) {
   return ((u + 1) * G - 1) / U;
 }
+// First unit of row block rb (units == nullptr: T units per row block).
+__host__ __device__ inline int64_t rb_first_unit(const int64_t* units, int64_t T, int64_t rb) {
+  return units ? units[rb] : rb * T;
+}
+// Row block holding unit u: the largest rb with rb_first_unit(rb) <= u.
+__host__ __device__ inline int64_t rb_of_unit(const int64_t* units, int64_t T, int64_t nrb, int64_t u) {
+  if (units == nullptr) return u / T;
+  int64_t lo = 0, hi = nrb - 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if (units[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+// Slot of workgroup w's partial state for row block rb.
+__host__ __device__ inline int64_t seg_slot(int64_t w, int64_t rb) { return w + rb; }
 
 inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 // Build the plan.  bf16: stream-K style partition over kPartitionCUs when the
 // plain one-workgroup-per-row-block launch would leave more than 10% of the
-// compute units idle in its last round.  f32: one workgroup per row-block.
-inline Plan make_plan(int B, int H, int n_q, int n_k, int d_c, int d_r, bool f32) {
+// compute units idle in its last round; chunk-causal calls always spread
+// their (uneven) units over kPartitionCUs workgroups.  f32: one workgroup per
+// row-block.  The workspace size does not depend on `vis`.
+inline Plan make_plan(int B, int H, int n_q, int n_k, int d_c, int d_r, bool f32,
+                      const Visibility* vis = nullptr) {
   Plan p{};
   p.B = B; p.H = H; p.n_q = n_q; p.n_k = n_k; p.d_c = d_c; p.width = d_c + d_r;
   p.rows_b = H * n_q;
   p.rb_per_b = (p.rows_b + kRowsPerBlock - 1) / kRowsPerBlock;
   p.rows_pad_b = p.rb_per_b * kRowsPerBlock;
   p.nrb = B * p.rb_per_b;
-  p.T = (n_k + key_tile(d_c) - 1) / key_tile(d_c);
+  const int bn = key_tile(d_c);
+  p.T = (n_k + bn - 1) / bn;
   p.U = (int64_t)p.nrb * p.T;
   p.elem = f32 ? 4 : 2;
   int64_t G = p.nrb;
@@ -81,15 +139,26 @@ inline Plan make_plan(int B, int H, int n_q, int n_k, int d_c, int d_r, bool f32
     if (eff < 0.9) G = rounds * kPartitionCUs;
     if (G > p.U) G = p.U;
   }
+  const int64_t g_slots = G > kPartitionCUs ? G : kPartitionCUs;   // covers the chunk-causal G too
+  if (!f32 && vis != nullptr && vis->chunk_len != 0) {
+    int64_t per_b = 0;
+    for (int rbl = 0; rbl < p.rb_per_b; ++rbl)
+      per_b += (vis->kv_max_of_block(rbl * kRowsPerBlock, n_k) + bn - 1) / bn;
+    p.U = (int64_t)B * per_b;
+    G = p.U < kPartitionCUs ? p.U : kPartitionCUs;
+    p.causal = true;
+  }
   p.G = (int32_t)G;
-  const int64_t slots = f32 ? (int64_t)p.nrb : 2 * G;
+  const int64_t slots = f32 ? (int64_t)p.nrb : g_slots + p.nrb;
   p.off_qt = 0;
   int64_t qt_bytes = (int64_t)B * p.rows_pad_b * p.width * p.elem;
   p.off_L = align_up(qt_bytes, 256);
   int64_t L_bytes = slots * kRowsPerBlock * (int64_t)d_c * 4;
   p.off_ml = align_up(p.off_L + L_bytes, 256);
   int64_t ml_bytes = slots * kRowsPerBlock * 2 * 4;
-  p.total = align_up(p.off_ml + ml_bytes, 256);
+  p.off_units = align_up(p.off_ml + ml_bytes, 256);
+  p.off_hdr = align_up(p.off_units + (int64_t)(p.nrb + 1) * 8, 256);
+  p.total = align_up(p.off_hdr + (int64_t)sizeof(PartitionHeader), 256);
   return p;
 }
 

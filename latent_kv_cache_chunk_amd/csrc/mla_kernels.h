@@ -30,6 +30,7 @@ struct AttendArgs {
   int64_t cache_bstride;  // elements between samples (capacity * width)
   void* workspace;
   float headroom;         // log2 headroom of the single-pass softmax (see attend.hip)
+  Visibility vis;         // chunk-causal key limits per query
 };
 
 struct UpprojArgs {

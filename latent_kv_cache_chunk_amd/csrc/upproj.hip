@@ -11,16 +11,12 @@
 
 namespace mla {
 
-// Slot holding row-block rb's segment produced by workgroup w (see Plan).
-__device__ inline int64_t seg_slot(int64_t w, int64_t rb, int64_t T, int64_t U, int64_t G) {
-  return (unit_begin(w, U, G) < rb * T) ? 2 * w + 1 : 2 * w;
-}
-
 template <int DC, bool OUT_F32>
 __global__ __launch_bounds__(256)
 void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restrict__ part_ml,
-                        int T, int64_t U, int G, int rb_per_b, int n_q, int H,
-                        const u16* __restrict__ w_uv, void* __restrict__ out) {
+                        const int64_t* __restrict__ units_ws, const PartitionHeader* __restrict__ hdr,
+                        int T, int rb_per_b, int n_q, int H, const u16* __restrict__ w_uv,
+                        void* __restrict__ out) {
   constexpr int DH = 128, KSTEPS = DC / 16;
   const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
@@ -30,16 +26,21 @@ void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restric
   const int64_t rb = (int64_t)b * rb_per_b + r / kRowsPerBlock;
   const int rl = r % kRowsPerBlock;
 
-  // Owners of this row-block's first and last unit; merge their segments.
-  const int64_t wa = unit_owner(rb * T, U, G), wb = unit_owner(rb * T + T - 1, U, G);
+  // The attention step's partition; owners of this row-block's first and
+  // last unit, whose segments are merged.
+  const PartitionHeader ph = *hdr;
+  const int64_t U = ph.U, G = ph.G;
+  const int64_t* units = ph.per_block_units ? units_ws : nullptr;
+  const int64_t u_first = rb_first_unit(units, T, rb), u_last = rb_first_unit(units, T, rb + 1) - 1;
+  const int64_t wa = unit_owner(u_first, U, G), wb = unit_owner(u_last, U, G);
   float M = -INFINITY;
   for (int64_t w = wa; w <= wb; ++w) {
-    const int64_t sl = seg_slot(w, rb, T, U, G);
+    const int64_t sl = seg_slot(w, rb);
     M = fmaxf(M, part_ml[(sl * kRowsPerBlock + rl) * 2]);
   }
   float lsum = 0.f;
   for (int64_t w = wa; w <= wb; ++w) {
-    const int64_t sl = seg_slot(w, rb, T, U, G);
+    const int64_t sl = seg_slot(w, rb);
     const float* ml = part_ml + (sl * kRowsPerBlock + rl) * 2;
     lsum += exp2f(ml[0] - M) * ml[1];
   }
@@ -55,7 +56,7 @@ void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restric
     const int c0 = ks * 16 + half * 8;
     float lc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int64_t w = wa; w <= wb; ++w) {
-      const int64_t sl = seg_slot(w, rb, T, U, G);
+      const int64_t sl = seg_slot(w, rb);
       const float wgt = exp2f(part_ml[(sl * kRowsPerBlock + rl) * 2] - M) * inv_l;
       const f32x4* src = reinterpret_cast<const f32x4*>(part_L + (sl * kRowsPerBlock + rl) * DC + c0);
       const f32x4 x0 = src[0], x1 = src[1];
@@ -122,11 +123,13 @@ hipError_t launch_upproj_bf16(const Plan& p, const UpprojArgs& a, hipStream_t s)
   char* ws = (char*)a.workspace;
   const float* L = (const float*)(ws + p.off_L);
   const float* ml = (const float*)(ws + p.off_ml);
+  const int64_t* units = (const int64_t*)(ws + p.off_units);
+  const PartitionHeader* hdr = (const PartitionHeader*)(ws + p.off_hdr);
   const u16* wv = (const u16*)a.w_uv;
   const dim3 grid(p.B * p.H, (p.n_q + 127) / 128), block(256);
 #define MLA_UPPROJ(DCV)                                                                                       \
-  if (a.out_f32) upproj_bf16_kernel<DCV, true><<<grid, block, 0, s>>>(L, ml, p.T, p.U, p.G, p.rb_per_b, p.n_q, p.H, wv, a.out); \
-  else upproj_bf16_kernel<DCV, false><<<grid, block, 0, s>>>(L, ml, p.T, p.U, p.G, p.rb_per_b, p.n_q, p.H, wv, a.out);
+  if (a.out_f32) upproj_bf16_kernel<DCV, true><<<grid, block, 0, s>>>(L, ml, units, hdr, p.T, p.rb_per_b, p.n_q, p.H, wv, a.out); \
+  else upproj_bf16_kernel<DCV, false><<<grid, block, 0, s>>>(L, ml, units, hdr, p.T, p.rb_per_b, p.n_q, p.H, wv, a.out);
   switch (p.d_c) {
     case 64: MLA_UPPROJ(64) break;
     case 128: MLA_UPPROJ(128) break;

@@ -26,14 +26,18 @@ MLA_BF16, MLA_F32 = 0, 1
 
 LIB_PATH = _LIB_PATH
 EXPORTED = ("mla_cache_append", "mla_chunk_attend_workspace_bytes", "mla_chunk_attend",
-            "mla_query_absorb", "mla_latent_attend", "mla_value_upproj",
-            "mla_status_string", "mla_last_error", "mla_version")
+            "mla_chunk_attend_causal", "mla_query_absorb", "mla_latent_attend", "mla_latent_attend_causal",
+            "mla_value_upproj", "mla_status_string", "mla_last_error", "mla_version")
 
 
 class MlaDims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("d_c", ctypes.c_int32), ("d_r", ctypes.c_int32), ("rope_t", ctypes.c_int32),
                 ("rope_h", ctypes.c_int32), ("rope_w", ctypes.c_int32), ("rope_theta", ctypes.c_double)]
+
+
+class MlaCausal(ctypes.Structure):
+    _fields_ = [("q_start", ctypes.c_int32), ("chunk_len", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -48,10 +52,16 @@ _lib.mla_chunk_attend_workspace_bytes.restype = _I64
 _lib.mla_chunk_attend.argtypes = [_DIMS, _I32, _I32, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32,
                                   ctypes.c_float, _P, _P, _I64, _P]
 _lib.mla_chunk_attend.restype = _I32
+_lib.mla_chunk_attend_causal.argtypes = [_DIMS, _I32, _I32, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32,
+                                         ctypes.POINTER(MlaCausal), ctypes.c_float, _P, _P, _I64, _P]
+_lib.mla_chunk_attend_causal.restype = _I32
 _lib.mla_query_absorb.argtypes = [_DIMS, _I32, _P, _P, _P, _I32, _P, ctypes.c_float, _I32, _P, _I64, _P]
 _lib.mla_query_absorb.restype = _I32
 _lib.mla_latent_attend.argtypes = [_DIMS, _I32, _P, _I32, _I32, _I32, _P, _I64, _P]
 _lib.mla_latent_attend.restype = _I32
+_lib.mla_latent_attend_causal.argtypes = [_DIMS, _I32, _P, _I32, _I32, _I32, ctypes.POINTER(MlaCausal), _P, _I64,
+                                          _P]
+_lib.mla_latent_attend_causal.restype = _I32
 _lib.mla_value_upproj.argtypes = [_DIMS, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P]
 _lib.mla_value_upproj.restype = _I32
 _lib.mla_status_string.argtypes = [_I32]
@@ -165,8 +175,12 @@ def _attend_checks(dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k):
 
 
 def chunk_attend(dims: Dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k: int, scale: float,
-                 out=None, out_dtype=None, workspace=None, stream=None) -> torch.Tensor:
-    """out[b,i,h] = sum_j softmax_j(scale*(q.k_h + RoPE(p_i)q_r.k_R)) W_UV[h] c_j over keys j < n_k."""
+                 out=None, out_dtype=None, workspace=None, stream=None, causal=None) -> torch.Tensor:
+    """out[b,i,h] = sum_j softmax_j(scale*(q.k_h + RoPE(p_i)q_r.k_R)) W_UV[h] c_j over the visible keys.
+
+    causal=None: every query sees keys [0, n_k).  causal=(q_start, chunk_len):
+    query i is token q_start + i and sees the keys of every chunk up to its own
+    (mla_chunk_attend_causal)."""
     n_q, dt = _attend_checks(dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k)
     odt = dt if out_dtype is None else out_dtype
     if out is None:
@@ -175,11 +189,16 @@ def chunk_attend(dims: Dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k: int, scale: 
     if workspace is None:
         workspace = alloc_workspace(dims, dt, n_q, n_k, q.device)
     d = dims.c()
-    code = _lib.mla_chunk_attend(ctypes.byref(d), _dtype_code(dt), _dtype_code(odt), q.data_ptr(), q_r.data_ptr(),
-                                 q_pos.data_ptr(), n_q, w_uk.data_ptr(), w_uv.data_ptr(), cache.data_ptr(),
-                                 cache.shape[1], int(n_k), float(scale), out.data_ptr(), workspace.data_ptr(),
-                                 workspace.numel(), _stream(stream))
-    _raise(code, "mla_chunk_attend")
+    args = (_dtype_code(dt), _dtype_code(odt), q.data_ptr(), q_r.data_ptr(), q_pos.data_ptr(), n_q,
+            w_uk.data_ptr(), w_uv.data_ptr(), cache.data_ptr(), cache.shape[1], int(n_k))
+    tail = (float(scale), out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream))
+    if causal is None:
+        code = _lib.mla_chunk_attend(ctypes.byref(d), *args, *tail)
+        _raise(code, "mla_chunk_attend")
+    else:
+        cz = MlaCausal(int(causal[0]), int(causal[1]))
+        code = _lib.mla_chunk_attend_causal(ctypes.byref(d), *args, ctypes.byref(cz), *tail)
+        _raise(code, "mla_chunk_attend_causal")
     return out
 
 
@@ -192,12 +211,17 @@ def query_absorb(dims: Dims, q, q_r, q_pos, w_uk, scale: float, n_k: int, worksp
     _raise(code, "mla_query_absorb")
 
 
-def latent_attend(dims: Dims, cache, n_q: int, n_k: int, workspace, stream=None) -> None:
+def latent_attend(dims: Dims, cache, n_q: int, n_k: int, workspace, stream=None, causal=None) -> None:
     _check(cache, "cache", (dims.batch, cache.shape[1], dims.d_c + dims.d_r), cache.dtype)
     d = dims.c()
-    code = _lib.mla_latent_attend(ctypes.byref(d), _dtype_code(cache.dtype), cache.data_ptr(), cache.shape[1],
-                                  int(n_q), int(n_k), workspace.data_ptr(), workspace.numel(), _stream(stream))
-    _raise(code, "mla_latent_attend")
+    args = (_dtype_code(cache.dtype), cache.data_ptr(), cache.shape[1], int(n_q), int(n_k))
+    tail = (workspace.data_ptr(), workspace.numel(), _stream(stream))
+    if causal is None:
+        _raise(_lib.mla_latent_attend(ctypes.byref(d), *args, *tail), "mla_latent_attend")
+    else:
+        cz = MlaCausal(int(causal[0]), int(causal[1]))
+        _raise(_lib.mla_latent_attend_causal(ctypes.byref(d), *args, ctypes.byref(cz), *tail),
+               "mla_latent_attend_causal")
 
 
 def value_upproj(dims: Dims, w_uv, out, n_q: int, n_k: int, workspace, stream=None) -> None:

@@ -45,6 +45,7 @@ class Workload:
     rope_split: Tuple[int, int, int] = (8, 12, 12)
     theta: float = 1e4
     d_model: int = 1536
+    chunk_tokens: int = 0             # > 0: queries span chunks of this many tokens (block-causal)
     notes: str = field(default="", compare=False)
 
     @property
@@ -74,20 +75,31 @@ class Workload:
     def with_batch(self, batch: int) -> "Workload":
         return replace(self, batch=batch, name=f"{self.name}_b{batch}")
 
-    # Algorithmic work of one chunk step (absorbed form, as computed).
+    @property
+    def causal(self):
+        """(q_start, chunk_len) of a block-causal call, or None (every key visible)."""
+        return (self.n_cached, self.chunk_tokens) if self.chunk_tokens else None
+
+    def visible_keys(self) -> int:
+        """Sum over the queries of the keys each one sees."""
+        if not self.chunk_tokens:
+            return self.n_q * self.n_k
+        i = np.arange(self.n_q, dtype=np.int64) + self.n_cached
+        return int(np.minimum(self.n_k, (i // self.chunk_tokens + 1) * self.chunk_tokens).sum())
+
+    # Algorithmic work of one chunk step (absorbed form, as computed; visible
+    # (query, key) pairs only).
     def attend_flops(self) -> float:
+        pairs = self.batch * self.n_heads * self.visible_keys()
         rows = self.batch * self.n_q * self.n_heads
-        return float(rows) * (self.n_k * (4 * self.d_c + 2 * self.d_r)
-                              + 4 * self.head_dim * self.d_c)
+        return float(pairs) * (4 * self.d_c + 2 * self.d_r) + float(rows) * 4 * self.head_dim * self.d_c
 
     def attend_core_flops(self) -> float:
         """Flops of the fused score/softmax/P.V kernel alone."""
-        rows = self.batch * self.n_q * self.n_heads
-        return float(rows) * self.n_k * (4 * self.d_c + 2 * self.d_r)
+        return float(self.batch * self.n_heads * self.visible_keys()) * (4 * self.d_c + 2 * self.d_r)
 
     def mha_equiv_flops(self) -> float:
-        rows = self.batch * self.n_q * self.n_heads
-        return float(rows) * self.n_k * (4 * self.head_dim + 2 * self.d_r)
+        return float(self.batch * self.n_heads * self.visible_keys()) * (4 * self.head_dim + 2 * self.d_r)
 
     def append_flops(self) -> float:
         return 2.0 * self.batch * self.n_q * self.d_model * (self.d_c + self.d_r)
@@ -107,8 +119,12 @@ WAN720P_LONG = Workload("wan720p_long", 1, (45, 80),
                         notes="frame 45x80, chunk 3 frames (10800 queries), "
                               "1 sink chunk + 6 recent chunks")
 DC_SWEEP = tuple(WAN480P.with_dc(d) for d in (64, 128, 192, 256))
+# Teacher-forcing form: all 21 latent frames of a 480P clip as queries, in 7
+# chunks of 3 frames, each chunk seeing itself and the earlier chunks.
+WAN480P_TF = Workload("wan480p_tf", 1, (30, 52), (), _frames(0, 21), chunk_tokens=3 * 30 * 52,
+                      notes="7 chunks of 4680 queries, block-causal")
 
-WORKLOADS = {w.name: w for w in (TINY, WAN480P, WAN480P_B8, WAN720P_LONG) + DC_SWEEP}
+WORKLOADS = {w.name: w for w in (TINY, WAN480P, WAN480P_B8, WAN720P_LONG, WAN480P_TF) + DC_SWEEP}
 
 
 def chunk_positions(frames, grid_hw) -> np.ndarray:

@@ -254,19 +254,22 @@ def chunk_attend(q, q_r, q_pos, w_uk, w_uv, cache, n_k: int, scale: float,
 
 
 def chunk_attend_rows(rows, q, q_r, q_pos, w_uk, w_uv, cache, n_k: int, scale: float,
-                      split=(8, 12, 12), theta: float = 1e4) -> np.ndarray:
-    """chunk_attend for a chosen set of output rows only (single-chunk form).
+                      split=(8, 12, 12), theta: float = 1e4,
+                      q_chunk=None, k_chunk=None) -> np.ndarray:
+    """chunk_attend for a chosen set of output rows only.
 
     rows: integer array [R, 3] of (b, i, h).  Returns [R, d_h] equal to
-    chunk_attend(...)[b, i, h, :] for each row; used at full workload sizes
-    where the whole output is too expensive for fp64 on the host.
+    chunk_attend(..., q_chunk, k_chunk)[b, i, h, :] for each row; used at
+    full workload sizes where the whole output is too expensive for fp64 on
+    the host.
     """
     rows = np.asarray(rows, dtype=np.int64)
     q, q_r_rot, w_uk, w_uv, c, kr = _prep(q, q_r, q_pos, w_uk, w_uv, cache, n_k, split, theta)
+    vis = _chunk_visibility(q_chunk, k_chunk, q.shape[1], n_k)
     out = np.empty((rows.shape[0], q.shape[-1]))
     for (b, h) in sorted({(int(r[0]), int(r[2])) for r in rows}):
         sel = np.nonzero((rows[:, 0] == b) & (rows[:, 2] == h))[0]
         q_h, k_h, v_h = _head_qkv(q, q_r_rot, w_uk, w_uv, c, kr, b, h)
         s = scale * (q_h[rows[sel, 1]] @ k_h.T)
-        out[sel] = attention_probs(s) @ v_h
+        out[sel] = attention_probs(s, None if vis is None else vis[rows[sel, 1]]) @ v_h
     return out

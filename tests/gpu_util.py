@@ -35,6 +35,12 @@ G1_MAX, G1_MEAN = 2e-2, 2e-3
 #   148-key shapes for d_c 64 and 192 over three seeds; mean errors 1.5-1.7e-3
 #   either way.
 G2_MAX, G2_MEAN = 3e-2, 2e-3
+#   Chunk-causal calls include rows that see only one chunk (down to a single
+#   key), where the bf16 roundings of q~ and P are not averaged over many keys.
+#   The same fp64 emulation on the tiny causal shapes (chunk 1, 48, 50; three
+#   seeds) gives normalised max errors of 0.019-0.041 and means of
+#   1.25-1.65e-3, so the max gate for these calls is 5e-2 (mean unchanged).
+G2_CAUSAL_MAX = 5e-2
 #   fp32 inputs, fp32 output, divided by the RMS of the reference output
 F32_MAX, F32_MEAN = 1e-4, 1e-5
 
@@ -46,10 +52,10 @@ def assert_g1(got, want, label=""):
     return e
 
 
-def assert_g2(got, want, label=""):
+def assert_g2(got, want, label="", max_norm=G2_MAX):
     e = errors(got, want)
     assert np.all(np.isfinite(got)), label
-    assert e["max_norm"] <= G2_MAX and e["mean_norm"] <= G2_MEAN, (label, e)
+    assert e["max_norm"] <= max_norm and e["mean_norm"] <= G2_MEAN, (label, e)
     return e
 
 

@@ -81,14 +81,17 @@ def test_invalid_sizes_and_dtypes():
 
 
 def test_workspace_plan_sizes():
-    # 480P: 56160 rows -> 220 row-blocks of 256; 512 key tiles; stream-K over 256 workgroups.
+    # 480P: 56160 rows -> 220 row-blocks of 256; 512 key tiles of 64; stream-K over 256 workgroups, whose
+    # partial states take one slot per (workgroup, row block) pair: fewer than 256 + 220.
     d = _dims()
     n480 = _ws(d, 0, 4680, 32760)
     rows_pad = 220 * 256
     qt = rows_pad * 224 * 2
-    slots = 2 * 256
-    assert n480 >= qt + slots * 256 * (192 + 2) * 4
-    assert n480 < qt + slots * 256 * (192 + 2) * 4 + 4096
+    slots = 256 + 220
+    states = slots * 256 * (192 + 2) * 4
+    units = (220 + 1) * 8
+    assert n480 >= qt + states + units
+    assert n480 < qt + states + units + 4096
     # fp32 variant: one slot per row-block
     n32 = _ws(d, 1, 48, 192)
     assert n32 >= 3 * 256 * 224 * 4 + 3 * 256 * 194 * 4
@@ -133,6 +136,24 @@ def test_calls_fail_validation_without_launching():
     assert lib.mla_value_upproj(ctypes.byref(d), 0, 5, 48, 192, fake, fake, fake, 1 << 40, None) == -2
     assert lib.mla_query_absorb(ctypes.byref(d), 0, fake, fake, fake, 48, fake, ctypes.c_float(0.1), 192,
                                 None, 1 << 40, None) == -3
+
+
+def test_causal_validation():
+    lib = mla.raw()
+    d = _dims()
+    fake = ctypes.c_void_p(0x10000)
+
+    def call(cz, n_q=48, n_k=192):
+        return lib.mla_chunk_attend_causal(ctypes.byref(d), 0, 0, fake, fake, fake, n_q, fake, fake, fake, 192, n_k,
+                                           cz, ctypes.c_float(0.08), fake, fake, 1 << 40, None)
+
+    assert call(None) == -1 and b"causal is null" in lib.mla_last_error()
+    assert call(ctypes.byref(mla.MlaCausal(0, 0))) == -1 and b"chunk_len" in lib.mla_last_error()
+    assert call(ctypes.byref(mla.MlaCausal(-1, 48))) == -1
+    assert call(ctypes.byref(mla.MlaCausal(150, 48))) == -1 and b"q_start" in lib.mla_last_error()
+    assert lib.mla_latent_attend_causal(ctypes.byref(d), 0, fake, 192, 48, 192, None, fake, 1 << 40, None) == -1
+    assert lib.mla_latent_attend_causal(ctypes.byref(d), 0, fake, 192, 48, 192,
+                                        ctypes.byref(mla.MlaCausal(144, 0)), fake, 1 << 40, None) == -1
 
 
 def test_binding_checks_tensors_on_host():

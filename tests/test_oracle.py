@@ -383,6 +383,23 @@ def test_selected_rows_match_full_output():
     np.testing.assert_allclose(got, full[rows[:, 0], rows[:, 1], rows[:, 2]], rtol=1e-13)
 
 
+def test_selected_rows_match_full_output_block_causal():
+    # row sampling must apply the same chunk-causal mask as the full output
+    p = _tiny_problem(seed=21, H=2, d_h=8, d_c=6, split=(8, 12, 12), n_q=9, n_k=12, B=1)
+    q_chunk = (3 + np.arange(9)) // 4          # queries are tokens 3..11 in chunks of 4
+    k_chunk = np.arange(12) // 4
+    full = oracle.chunk_attend(p["q"], p["q_r"], p["q_pos"], p["w_uk"], p["w_uv"], p["cache"], p["n_k"],
+                               p["scale"], q_chunk=q_chunk, k_chunk=k_chunk)
+    rows = np.array([[0, 0, 0], [0, 8, 1], [0, 4, 1], [0, 5, 0]])
+    got = oracle.chunk_attend_rows(rows, p["q"], p["q_r"], p["q_pos"], p["w_uk"], p["w_uv"], p["cache"],
+                                   p["n_k"], p["scale"], q_chunk=q_chunk, k_chunk=k_chunk)
+    np.testing.assert_allclose(got, full[rows[:, 0], rows[:, 1], rows[:, 2]], rtol=1e-13)
+    # and the mask is live: the unmasked rows differ
+    open_rows = oracle.chunk_attend_rows(rows, p["q"], p["q_r"], p["q_pos"], p["w_uk"], p["w_uv"], p["cache"],
+                                         p["n_k"], p["scale"])
+    assert np.abs(open_rows - got).max() > 1e-3
+
+
 def test_exponential_tilting_of_gaussian_latent():
     # With c ~ N(0, I) and scores a.c, the softmax-weighted mean of c tends
     # to a (mean of the exponentially tilted Gaussian).  So O -> w_uv (alpha w_uk^T q).
