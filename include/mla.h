@@ -187,6 +187,55 @@ int32_t mla_value_upproj(const mla_dims* dims, int32_t dtype, int32_t out_dtype,
                          int32_t n_q, int32_t n_k, const void* w_uv, void* out,
                          void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Rolling latent cache for long rollouts (a fixed-size sliding window of
+ * cached chunks: VideoMLA arXiv abstract), with `sink_chunks` leading
+ * chunks kept for the whole rollout.  Host-side bookkeeping only; the cache
+ * itself is the caller's [B, capacity, d_c + d_r] buffer.
+ *   capacity = (sink_chunks + window_chunks + 1) * chunk_tokens
+ * Chunk j (0-based) goes to chunk slot j while the ring fills; afterwards
+ * chunk j >= sink_chunks goes to chunk slot
+ * sink_chunks + (j - sink_chunks) mod (window_chunks + 1), the slot the
+ * oldest window chunk leaves when chunk j-1 is committed.  The key range of
+ * every step is slots [0, n_k), in slot order; attention does not depend on
+ * key order and positional keys keep their absolute positions, so nothing
+ * is moved.  All batch samples advance together. */
+typedef struct mla_ring {
+  int32_t chunk_tokens;
+  int32_t sink_chunks;
+  int32_t window_chunks;
+  int32_t capacity;      /* cache slots the ring needs */
+  int64_t committed;     /* chunks committed so far = index of the current chunk */
+} mla_ring;
+
+/* Initialize an empty ring.  chunk_tokens >= 1, sink_chunks >= 0,
+ * window_chunks >= 0. */
+int32_t mla_ring_init(mla_ring* ring, int32_t chunk_tokens, int32_t sink_chunks, int32_t window_chunks);
+
+/* Where the current chunk goes and which keys its steps attend to: append
+ * its tokens with mla_cache_append(..., write_offset), then attend with
+ * n_k keys (every cached chunk plus the current one).  Repeated denoising
+ * steps of the same chunk overwrite the same slots. */
+int32_t mla_ring_current(const mla_ring* ring, int32_t* write_offset, int32_t* n_k);
+
+/* The current chunk's last denoising step is done: it joins the cache (the
+ * oldest non-sink chunk leaves if the window is full). */
+int32_t mla_ring_commit(mla_ring* ring);
+
+/* Host array [sink_chunks + window_chunks + 1]: the chunk index held by each
+ * chunk slot (the current chunk included), or -1 for an empty slot. */
+int32_t mla_ring_slot_chunks(const mla_ring* ring, int64_t* chunk_of_slot);
+
+/* Bytes of a latent cache of `capacity` slots for all B samples (one layer),
+ * and of the dense per-head K and V cache it replaces (2 * H * d_h values
+ * per token; VideoMLA atlas.scime.ai summary, "Key results": 224 against 3072
+ * scalars per token at d_c = 192).  Negative mla_status on invalid
+ * arguments. */
+int64_t mla_cache_bytes(const mla_dims* dims, int32_t dtype, int32_t capacity);
+int64_t mla_dense_kv_bytes(const mla_dims* dims, int32_t dtype, int32_t capacity);
+
+/* Reason for the last failed mla_ring_* or byte-count call on this thread. */
+const char* mla_ring_last_error(void);
+
 /* Static description of a status code. */
 const char* mla_status_string(int32_t status);
 

@@ -27,7 +27,9 @@ MLA_BF16, MLA_F32 = 0, 1
 LIB_PATH = _LIB_PATH
 EXPORTED = ("mla_cache_append", "mla_chunk_attend_workspace_bytes", "mla_chunk_attend",
             "mla_chunk_attend_causal", "mla_query_absorb", "mla_latent_attend", "mla_latent_attend_causal",
-            "mla_value_upproj", "mla_status_string", "mla_last_error", "mla_version")
+            "mla_value_upproj", "mla_status_string", "mla_last_error", "mla_version",
+            "mla_ring_init", "mla_ring_current", "mla_ring_commit", "mla_ring_slot_chunks",
+            "mla_cache_bytes", "mla_dense_kv_bytes", "mla_ring_last_error")
 
 
 class MlaDims(ctypes.Structure):
@@ -38,6 +40,11 @@ class MlaDims(ctypes.Structure):
 
 class MlaCausal(ctypes.Structure):
     _fields_ = [("q_start", ctypes.c_int32), ("chunk_len", ctypes.c_int32)]
+
+
+class MlaRing(ctypes.Structure):
+    _fields_ = [("chunk_tokens", ctypes.c_int32), ("sink_chunks", ctypes.c_int32),
+                ("window_chunks", ctypes.c_int32), ("capacity", ctypes.c_int32), ("committed", ctypes.c_int64)]
 
 
 _P = ctypes.c_void_p
@@ -64,6 +71,21 @@ _lib.mla_latent_attend_causal.argtypes = [_DIMS, _I32, _P, _I32, _I32, _I32, cty
 _lib.mla_latent_attend_causal.restype = _I32
 _lib.mla_value_upproj.argtypes = [_DIMS, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P]
 _lib.mla_value_upproj.restype = _I32
+_RING = ctypes.POINTER(MlaRing)
+_lib.mla_ring_init.argtypes = [_RING, _I32, _I32, _I32]
+_lib.mla_ring_init.restype = _I32
+_lib.mla_ring_current.argtypes = [_RING, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]
+_lib.mla_ring_current.restype = _I32
+_lib.mla_ring_commit.argtypes = [_RING]
+_lib.mla_ring_commit.restype = _I32
+_lib.mla_ring_slot_chunks.argtypes = [_RING, ctypes.POINTER(_I64)]
+_lib.mla_ring_slot_chunks.restype = _I32
+_lib.mla_cache_bytes.argtypes = [_DIMS, _I32, _I32]
+_lib.mla_cache_bytes.restype = _I64
+_lib.mla_dense_kv_bytes.argtypes = [_DIMS, _I32, _I32]
+_lib.mla_dense_kv_bytes.restype = _I64
+_lib.mla_ring_last_error.argtypes = []
+_lib.mla_ring_last_error.restype = ctypes.c_char_p
 _lib.mla_status_string.argtypes = [_I32]
 _lib.mla_status_string.restype = ctypes.c_char_p
 _lib.mla_last_error.argtypes = []
@@ -232,6 +254,50 @@ def value_upproj(dims: Dims, w_uv, out, n_q: int, n_k: int, workspace, stream=No
                                  int(n_k), w_uv.data_ptr(), out.data_ptr(), workspace.data_ptr(),
                                  workspace.numel(), _stream(stream))
     _raise(code, "mla_value_upproj")
+
+
+class Ring:
+    """Rolling latent cache bookkeeping (mla_ring_*): sink chunks kept for the
+    whole rollout, a window of recent chunks, one slot for the current chunk."""
+
+    def __init__(self, chunk_tokens: int, sink_chunks: int, window_chunks: int):
+        self._r = MlaRing()
+        code = _lib.mla_ring_init(ctypes.byref(self._r), int(chunk_tokens), int(sink_chunks), int(window_chunks))
+        if code != MLA_OK:
+            raise ValueError(_lib.mla_ring_last_error().decode())
+
+    @property
+    def capacity(self) -> int:
+        return self._r.capacity
+
+    @property
+    def committed(self) -> int:
+        return self._r.committed
+
+    def current(self):
+        """(write_offset, n_k) of the chunk being denoised."""
+        off, n_k = _I32(), _I32()
+        _raise(_lib.mla_ring_current(ctypes.byref(self._r), ctypes.byref(off), ctypes.byref(n_k)), "mla_ring_current")
+        return off.value, n_k.value
+
+    def commit(self) -> None:
+        _raise(_lib.mla_ring_commit(ctypes.byref(self._r)), "mla_ring_commit")
+
+    def slot_chunks(self):
+        n = self._r.sink_chunks + self._r.window_chunks + 1
+        arr = (_I64 * n)()
+        _raise(_lib.mla_ring_slot_chunks(ctypes.byref(self._r), arr), "mla_ring_slot_chunks")
+        return list(arr)
+
+
+def cache_bytes(dims: Dims, dtype: torch.dtype, capacity: int) -> int:
+    d = dims.c()
+    return int(_lib.mla_cache_bytes(ctypes.byref(d), _dtype_code(dtype), int(capacity)))
+
+
+def dense_kv_bytes(dims: Dims, dtype: torch.dtype, capacity: int) -> int:
+    d = dims.c()
+    return int(_lib.mla_dense_kv_bytes(ctypes.byref(d), _dtype_code(dtype), int(capacity)))
 
 
 def raw():

@@ -1,0 +1,74 @@
+"""A rolling rollout through the ring cache on the GPU: every chunk is
+appended into the slots mla_ring_current hands out (twice, as two denoising
+steps), attended over [0, n_k), and committed.
+
+The oracle never sees the ring: it rebuilds the visible key set in chunk
+order -- the sink chunk, the most recent window chunks, the current chunk --
+from its own append of those chunks' hidden states, and runs plain attention
+over it.  A wrong slot, a stale chunk or a wrong n_k changes the keys and
+fails the comparison; key order does not matter to softmax (pinned in
+tests/test_oracle.py), which is why the ring may keep them in slot order.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from latent_kv_cache_chunk_amd import synth
+from tests.gpu_util import assert_g2, need_gpu, np64
+
+pytestmark = pytest.mark.gpu
+
+GRID = (4, 6)
+FRAMES_PER_CHUNK = 2
+C = GRID[0] * GRID[1] * FRAMES_PER_CHUNK          # 48 tokens per chunk
+SINK, WINDOW, CHUNKS = 1, 2, 7
+
+
+def _bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16)
+
+
+def test_rolling_rollout_matches_oracle():
+    mla = need_gpu()
+    dims = mla.Dims(batch=1)
+    ring = mla.Ring(C, SINK, WINDOW)
+    cap = ring.capacity
+    rng = np.random.default_rng(11)
+    D, H, dh, dc, dr = 1536, 12, 128, 192, 32
+    w_dkv = _bf16(rng.standard_normal((dc, D), np.float32) / np.sqrt(D))
+    w_kr = _bf16(rng.standard_normal((dr, D), np.float32) / np.sqrt(D))
+    w_uk = _bf16(rng.standard_normal((H, dh, dc), np.float32) / np.sqrt(dc))
+    w_uv = _bf16(rng.standard_normal((H, dh, dc), np.float32) / np.sqrt(dc))
+    scale = 1.0 / np.sqrt(dh + dr)
+    cache = torch.zeros((1, cap, dc + dr), dtype=torch.bfloat16, device="cuda")
+    dev = lambda t: t.cuda()
+    rows_of = {}                                   # chunk -> oracle cache rows (fp64 of the bf16 rounding)
+    for j in range(CHUNKS):
+        off, n_k = ring.current()
+        pos = torch.from_numpy(synth.chunk_positions(range(FRAMES_PER_CHUNK * j, FRAMES_PER_CHUNK * (j + 1)), GRID))
+        q = _bf16(rng.standard_normal((1, C, H, dh), np.float32))
+        q_r = _bf16(rng.standard_normal((1, C, H, dr), np.float32))
+        for step in range(2):                      # two denoising steps overwrite the same slots
+            x = _bf16(rng.standard_normal((1, C, D), np.float32))
+            mla.cache_append(dims, dev(x), dev(w_dkv), dev(w_kr), dev(pos), cache, off)
+            out = mla.chunk_attend(dims, dev(q), dev(q_r), dev(pos), dev(w_uk), dev(w_uv), cache, n_k, scale,
+                                   out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            rows_of[j] = oracle.bf16_rne(oracle.latent_rows(np64(x), np64(w_dkv), np64(w_kr), pos.numpy()))[0]
+            # the visible set in chunk order: sinks, the last WINDOW committed chunks, the current chunk
+            visible = sorted(set(range(min(SINK, j + 1))) | set(range(max(SINK, j - WINDOW), j + 1)))
+            keys = np.concatenate([rows_of[c] for c in visible], 0)[None]
+            assert n_k == keys.shape[1], (j, n_k, visible)
+            want = oracle.chunk_attend(np64(q), np64(q_r), pos.numpy(), np64(w_uk), np64(w_uv), keys, n_k, scale)
+            assert_g2(np64(out), want, f"chunk {j} step {step}")
+        # the ring's slot map says where each chunk is; its rows must be there
+        slots = ring.slot_chunks()
+        got_cache = np64(cache)[0]
+        for s, c in enumerate(slots):
+            if c >= 0:
+                np.testing.assert_allclose(got_cache[s * C:(s + 1) * C], rows_of[c], rtol=1e-2, atol=1e-2,
+                                           err_msg=f"slot {s} should hold chunk {c}")
+        ring.commit()
+    assert ring.current()[1] == cap                 # the window is full: every slot is live
