@@ -38,4 +38,6 @@ from .mla_oracle import (  # noqa: F401
     attention_probs,
     chunk_attend,
     chunk_attend_rows,
+    mha_attend,
+    mha_attend_rows,
 )

@@ -273,3 +273,49 @@ def chunk_attend_rows(rows, q, q_r, q_pos, w_uk, w_uv, cache, n_k: int, scale: f
         s = scale * (q_h[rows[sel, 1]] @ k_h.T)
         out[sel] = attention_probs(s, None if vis is None else vis[rows[sel, 1]]) @ v_h
     return out
+
+
+def mha_attend(q, k, v, n_k: int, scale: float, q_chunk=None, k_chunk=None,
+               block_rows: int = 512) -> np.ndarray:
+    """Standard multi-head attention over per-head keys and values.
+
+    The dense per-head K/V cache that the latent cache replaces (VideoMLA
+    atlas.scime.ai summary, "Key results": 2 x H x d_h cached values per
+    token).  q [B, Nq, H, d], k and v [B, cap, H, d] (positional encoding, if
+    any, already applied); the first n_k key slots are visible, optionally
+    restricted by chunk indices as in chunk_attend.  Per (b, h):
+        O = softmax(scale * Q K^T, mask) V.
+    Returns O [B, Nq, H, d_v].
+
+    Pinned by: brute-force scalar loops, torch's CPU fp64
+    scaled_dot_product_attention, q = 0 giving the plain mean of V, and the
+    identity with chunk_attend when K, V are the per-head keys and values
+    reconstructed from a latent cache (tests/test_oracle.py).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)[:, :n_k]
+    v = np.asarray(v, dtype=np.float64)[:, :n_k]
+    B, n_q, H, _ = q.shape
+    vis = _chunk_visibility(q_chunk, k_chunk, n_q, n_k)
+    out = np.empty((B, n_q, H, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            for i0 in range(0, n_q, block_rows):
+                i1 = min(n_q, i0 + block_rows)
+                s = scale * (q[b, i0:i1, h] @ k[b, :, h].T)
+                p = attention_probs(s, None if vis is None else vis[i0:i1])
+                out[b, i0:i1, h, :] = p @ v[b, :, h]
+    return out
+
+
+def mha_attend_rows(rows, q, k, v, n_k: int, scale: float) -> np.ndarray:
+    """mha_attend for chosen output rows (b, i, h) only: [R, d_v], each equal
+    to mha_attend(q, k, v, n_k, scale)[b, i, h]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.empty((rows.shape[0], np.shape(v)[-1]))
+    for r, (b, i, h) in enumerate(rows):
+        qv = np.asarray(q[b, i, h], dtype=np.float64)
+        kk = np.asarray(k[b, :n_k, h], dtype=np.float64)
+        vv = np.asarray(v[b, :n_k, h], dtype=np.float64)
+        out[r] = attention_probs(scale * (kk @ qv)) @ vv
+    return out

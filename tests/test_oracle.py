@@ -418,6 +418,92 @@ def test_exponential_tilting_of_gaussian_latent():
 
 
 # --------------------------------------------------------------------------
+# Dense per-head attention (the K/V cache the latent replaces)
+# --------------------------------------------------------------------------
+
+def _mha_problem(seed, B=2, n_q=3, n_k=5, H=2, d=4, dv=3, cap_extra=2):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, n_q, H, d)), rng.standard_normal((B, n_k + cap_extra, H, d)),
+            rng.standard_normal((B, n_k + cap_extra, H, dv)), n_k)
+
+
+def _mha_brute(q, k, v, n_k, scale, q_chunk=None, k_chunk=None):
+    """Scalar loops over Python floats."""
+    B, n_q, H, d = q.shape
+    out = np.zeros((B, n_q, H, v.shape[-1]))
+    for b in range(B):
+        for i in range(n_q):
+            for h in range(H):
+                js = [j for j in range(n_k) if q_chunk is None or k_chunk[j] <= q_chunk[i]]
+                sc = [scale * sum(float(q[b, i, h, e]) * float(k[b, j, h, e]) for e in range(d)) for j in js]
+                m = max(sc)
+                w = [math.exp(x - m) for x in sc]
+                for e in range(v.shape[-1]):
+                    out[b, i, h, e] = sum(w[t] * float(v[b, js[t], h, e]) for t in range(len(js))) / sum(w)
+    return out
+
+
+def test_mha_matches_brute_force():
+    for seed in range(3):
+        q, k, v, n_k = _mha_problem(30 + seed)
+        np.testing.assert_allclose(oracle.mha_attend(q, k, v, n_k, 0.41), _mha_brute(q, k, v, n_k, 0.41),
+                                   rtol=1e-12, atol=1e-13)
+    q, k, v, n_k = _mha_problem(33, n_q=4, n_k=6)
+    qc, kc = [0, 0, 1, 1], [0, 0, 0, 1, 1, 2]
+    np.testing.assert_allclose(oracle.mha_attend(q, k, v, n_k, 0.41, q_chunk=qc, k_chunk=kc),
+                               _mha_brute(q, k, v, n_k, 0.41, q_chunk=qc, k_chunk=kc), rtol=1e-12, atol=1e-13)
+
+
+def test_mha_matches_torch_sdpa():
+    q, k, v, n_k = _mha_problem(34, B=2, n_q=9, n_k=31, H=3, d=16, dv=16)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a[:, :n_k] if a is not q else a)).permute(0, 2, 1, 3)
+    want = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), scale=0.2)
+    np.testing.assert_allclose(oracle.mha_attend(q, k, v, n_k, 0.2), want.permute(0, 2, 1, 3).numpy(),
+                               rtol=1e-11, atol=1e-12)
+
+
+def test_mha_zero_query_gives_mean_of_values():
+    q, k, v, n_k = _mha_problem(35, n_k=11)
+    got = oracle.mha_attend(np.zeros_like(q), k, v, n_k, 0.5)
+    for i in range(q.shape[1]):
+        np.testing.assert_allclose(got[:, i], v[:, :n_k].mean(1), rtol=1e-12, atol=1e-13)
+
+
+def test_mha_on_reconstructed_kv_equals_latent_attention():
+    """The non-absorbed MLA definition is dense attention over
+    K_h = [C W_UK[h]^T || RoPE'd k_R] and V_h = C W_UV[h]^T."""
+    p = _tiny_problem(seed=36, H=3, d_h=8, d_c=6, split=(8, 12, 12), n_q=5, n_k=17, B=2)
+    d_c, n_k = 6, p["n_k"]
+    c, kr = p["cache"][:, :, :d_c], p["cache"][:, :, d_c:]
+    k = np.concatenate([np.einsum("bjc,hdc->bjhd", c, p["w_uk"]),
+                        np.broadcast_to(kr[:, :, None], kr.shape[:2] + (3, kr.shape[-1]))], -1)
+    v = np.einsum("bjc,hdc->bjhd", c, p["w_uv"])
+    qq = np.concatenate([p["q"], oracle.rope3d(p["q_r"], p["q_pos"][None, :, None, :])], -1)
+    np.testing.assert_allclose(oracle.mha_attend(qq, k, v, n_k, p["scale"]), _oracle(p), rtol=1e-11, atol=1e-12)
+
+
+def test_mha_selected_rows_match_full_output():
+    q, k, v, n_k = _mha_problem(37, B=2, n_q=6, n_k=13, H=3, d=8, dv=5)
+    full = oracle.mha_attend(q, k, v, n_k, 0.3)
+    rows = np.array([[0, 0, 0], [1, 5, 2], [0, 3, 1], [1, 2, 0]])
+    np.testing.assert_allclose(oracle.mha_attend_rows(rows, q, k, v, n_k, 0.3),
+                               full[rows[:, 0], rows[:, 1], rows[:, 2]], rtol=1e-13)
+
+
+@pytest.mark.parametrize("mutation", ["kv_swapped", "keys_past_n_k", "head_mixed"])
+def test_mha_planted_mistakes_are_caught(mutation):
+    q, k, v, n_k = _mha_problem(38, B=1, n_q=3, n_k=5, H=2, d=4, dv=4)
+    want = _mha_brute(q, k, v, n_k, 0.41)
+    if mutation == "kv_swapped":
+        got = oracle.mha_attend(q, v, k, n_k, 0.41)
+    elif mutation == "keys_past_n_k":
+        got = oracle.mha_attend(q, k, v, n_k + 2, 0.41)
+    else:
+        got = oracle.mha_attend(q, k[:, :, ::-1], v, n_k, 0.41)
+    assert not np.allclose(got, want, rtol=1e-6, atol=1e-6), mutation
+
+
+# --------------------------------------------------------------------------
 # Planted mistakes: each one must be caught by a pin above.
 # --------------------------------------------------------------------------
 
