@@ -187,6 +187,50 @@ int32_t mla_value_upproj(const mla_dims* dims, int32_t dtype, int32_t out_dtype,
                          int32_t n_q, int32_t n_k, const void* w_uv, void* out,
                          void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Standard multi-head attention over per-head keys and values: the dense
+ * K/V cache the latent cache replaces (2 * H * d_h values per token against
+ * d_c + d_r; VideoMLA atlas.scime.ai summary, "Key results"), provided as
+ * the comparison point for the latent path.  For every (b, i, h):
+ *   out[b,i,h,:] = sum_j softmax_j(softmax_scale * q[b,i,h,:] . k[b,j,h,:]) v[b,j,h,:]
+ * over keys j = 0 .. n_k-1 (all visible: one chunk of queries that sees every
+ * cached chunk and itself).  Positional encoding, if any, is already applied
+ * to q and k.
+ *   q    device bf16 [B, n_q, H, head_dim]
+ *   k, v device bf16 [B, cache_capacity, H, head_dim]; slots 0 .. n_k-1 are read
+ *   out  device [B, n_q, H, head_dim] of out_dtype (MLA_BF16 or MLA_F32)
+ *   workspace device, at least mla_mha_attend_workspace_bytes(...) bytes.
+ * Scores and P.V use bf16 MFMA with fp32 accumulation; the softmax is fp32
+ * in base 2, with softmax_scale*log2(e) applied to the fp32 scores (q is
+ * used as given, never rescaled and re-rounded); P is rounded to bf16.
+ * Supported: head_dim = 128, 1 <= n_q <= n_k <= cache_capacity,
+ * cache_capacity * n_heads * 256 < 2^32.  Errors as for mla_chunk_attend. */
+int64_t mla_mha_attend_workspace_bytes(int32_t batch, int32_t n_heads, int32_t head_dim,
+                                       int32_t n_q, int32_t n_k);
+int32_t mla_mha_attend(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t out_dtype,
+                       const void* q, int32_t n_q,
+                       const void* k, const void* v, int32_t cache_capacity, int32_t n_k,
+                       float softmax_scale, void* out,
+                       void* workspace, int64_t workspace_bytes, void* stream);
+
+/* mla_chunk_attend in the non-absorbed form of multi-head latent attention
+ * (DeepSeek-V2, listed under "Builds on" on both VideoMLA pages): per-head
+ * keys and values are first materialised from the latent cache,
+ *   K_h[j] = [W_UK[h] c_j || k_R,j]   (d_h + d_r),   V_h[j] = W_UV[h] c_j,
+ * each rounded once to bf16 (fp32 accumulation), into the workspace; then
+ * the attention of mla_mha_attend runs with queries [q_h || RoPE3D(p_i) q_r,h]
+ * (the rotated part rounded once to bf16).
+ * Same function as mla_chunk_attend up to rounding; it trades the absorbed
+ * form's wider scores (d_c + d_r per key) for per-head K/V traffic.
+ * Arguments as for mla_chunk_attend with in_dtype MLA_BF16.  Supported:
+ * the mla_dims of mla_chunk_attend, n_k * n_heads * 320 < 2^32. */
+int64_t mla_chunk_attend_expanded_workspace_bytes(const mla_dims* dims, int32_t n_q, int32_t n_k);
+int32_t mla_chunk_attend_expanded(const mla_dims* dims, int32_t out_dtype,
+                                  const void* q, const void* q_r, const int32_t* q_pos, int32_t n_q,
+                                  const void* w_uk, const void* w_uv,
+                                  const void* cache, int32_t cache_capacity, int32_t n_k,
+                                  float softmax_scale, void* out,
+                                  void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Rolling latent cache for long rollouts (a fixed-size sliding window of
  * cached chunks: VideoMLA arXiv abstract), with `sink_chunks` leading
  * chunks kept for the whole rollout.  Host-side bookkeeping only; the cache

@@ -24,7 +24,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla_hip.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "append.hip", "absorb.hip", "attend.hip", "attend_wide.hip", "upproj.hip", "cache_ring.hip"]
+SOURCES = ["api.hip", "append.hip", "absorb.hip", "attend.hip", "attend_wide.hip", "attend_mha.hip", "upproj.hip",
+           "cache_ring.hip"]
 
 
 def hipcc() -> str:

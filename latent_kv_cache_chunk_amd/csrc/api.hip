@@ -199,9 +199,119 @@ int32_t chunk_attend_impl(const mla_dims* dims, int32_t in_dtype, int32_t out_dt
     return st;
   return do_upproj(in_dtype, out_dtype, p, w_uv, out, workspace, s);
 }
+
+// ---------------------------------------------------------------------------
+// Standard attention over per-head K/V (dense baseline, non-absorbed form).
+// ---------------------------------------------------------------------------
+int32_t check_mha_sizes(int32_t batch, int32_t n_heads, int32_t n_q, int32_t n_k, int32_t dqk) {
+  if (batch < 1 || n_heads < 1) return fail(MLA_ERR_INVALID_ARG, "batch and n_heads must be >= 1");
+  if (n_heads > 4096) return fail(MLA_ERR_UNSUPPORTED, "n_heads must be <= 4096 (got %d)", n_heads);
+  if (n_q < 1) return fail(MLA_ERR_INVALID_ARG, "n_q must be >= 1 (got %d)", n_q);
+  if (n_k < n_q) return fail(MLA_ERR_INVALID_ARG, "n_k (%d) must be >= n_q (%d): the current chunk is part of the keys", n_k, n_q);
+  if ((int64_t)batch * n_heads * ((int64_t)n_q + 255) > (int64_t)1 << 30)
+    return fail(MLA_ERR_UNSUPPORTED, "batch * n_heads * n_q too large");
+  if ((int64_t)batch * n_k > (int64_t)1 << 30) return fail(MLA_ERR_UNSUPPORTED, "batch * n_k too large");
+  (void)dqk;
+  return MLA_OK;
+}
+
+int32_t check_mha_capacity(int32_t n_heads, int32_t n_k, int32_t cap, int32_t dqk) {
+  if (n_k > cap) return fail(MLA_ERR_INVALID_ARG, "n_k (%d) exceeds cache_capacity (%d)", n_k, cap);
+  // key offsets inside one (batch, head) are 32-bit
+  if ((int64_t)cap * n_heads * dqk * 2 >= (int64_t)1 << 32)
+    return fail(MLA_ERR_UNSUPPORTED, "cache_capacity * n_heads too large (one sample's K must stay below 4 GiB)");
+  return MLA_OK;
+}
+
+int32_t check_mha_workspace(const mla::MhaPlan& p, const void* ws, int64_t bytes) {
+  if (ws == nullptr) return fail(MLA_ERR_WORKSPACE, "workspace is null");
+  if (!aligned(ws, 256)) return fail(MLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (bytes < p.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace has %lld bytes, %lld needed", (long long)bytes, (long long)p.total);
+  return MLA_OK;
+}
+
+int32_t do_mha_attend(const mla::MhaPlan& p, const void* k, const void* v, int64_t cap, float scale, int32_t out_dtype,
+                      void* out, void* ws, hipStream_t s, const char* what) {
+  mla::MhaAttendArgs a{};
+  a.k = k; a.v = v; a.cap = cap; a.headroom = attend_headroom();
+  a.qscale = (float)((double)scale * mla::kLog2e);
+  a.out = out; a.out_f32 = out_dtype == MLA_F32; a.workspace = ws;
+  return finish(mla::launch_mha_attend(p, a, s), s, what);
+}
+
 }  // namespace
 
 extern "C" {
+
+int64_t mla_mha_attend_workspace_bytes(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t n_q, int32_t n_k) {
+  if (head_dim != 128) return fail(MLA_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+  int32_t st = check_mha_sizes(batch, n_heads, n_q, n_k, 128);
+  if (st) return st;
+  return mla::make_mha_plan(batch, n_heads, n_q, n_k, 128, false).total;
+}
+
+int32_t mla_mha_attend(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t out_dtype, const void* q,
+                       int32_t n_q, const void* k, const void* v, int32_t cache_capacity, int32_t n_k,
+                       float softmax_scale, void* out, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (head_dim != 128) return fail(MLA_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+  int32_t st = check_mha_sizes(batch, n_heads, n_q, n_k, 128);
+  if (st) return st;
+  if ((st = check_dtype(out_dtype, "out_dtype"))) return st;
+  if ((st = check_ptr(q, "q"))) return st;
+  if ((st = check_ptr(k, "k"))) return st;
+  if ((st = check_ptr(v, "v"))) return st;
+  if ((st = check_ptr(out, "out"))) return st;
+  if ((st = check_mha_capacity(n_heads, n_k, cache_capacity, 128))) return st;
+  if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  const mla::MhaPlan p = mla::make_mha_plan(batch, n_heads, n_q, n_k, 128, false);
+  if ((st = check_mha_workspace(p, workspace, workspace_bytes))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  mla::MhaQueryArgs qa{};
+  qa.q = q; qa.workspace = workspace;
+  if ((st = finish(mla::launch_mha_prep_q(p, qa, s), s, "mla_mha_attend"))) return st;
+  return do_mha_attend(p, k, v, cache_capacity, softmax_scale, out_dtype, out, workspace, s, "mla_mha_attend");
+}
+
+int64_t mla_chunk_attend_expanded_workspace_bytes(const mla_dims* dims, int32_t n_q, int32_t n_k) {
+  int32_t st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_mha_sizes(dims->batch, dims->n_heads, n_q, n_k, 160))) return st;
+  return mla::make_mha_plan(dims->batch, dims->n_heads, n_q, n_k, 160, true).total;
+}
+
+int32_t mla_chunk_attend_expanded(const mla_dims* dims, int32_t out_dtype, const void* q, const void* q_r,
+                                  const int32_t* q_pos, int32_t n_q, const void* w_uk, const void* w_uv,
+                                  const void* cache, int32_t cache_capacity, int32_t n_k, float softmax_scale,
+                                  void* out, void* workspace, int64_t workspace_bytes, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_mha_sizes(dims->batch, dims->n_heads, n_q, n_k, 160))) return st;
+  if ((st = check_dtype(out_dtype, "out_dtype"))) return st;
+  if ((st = check_ptr(q, "q"))) return st;
+  if ((st = check_ptr(q_r, "q_r"))) return st;
+  if ((st = check_ptr(q_pos, "q_pos", 4))) return st;
+  if ((st = check_ptr(w_uk, "w_uk"))) return st;
+  if ((st = check_ptr(w_uv, "w_uv"))) return st;
+  if ((st = check_ptr(cache, "cache"))) return st;
+  if ((st = check_ptr(out, "out"))) return st;
+  if (n_k > cache_capacity) return fail(MLA_ERR_INVALID_ARG, "n_k (%d) exceeds cache_capacity (%d)", n_k, cache_capacity);
+  if ((st = check_mha_capacity(dims->n_heads, n_k, n_k, 160))) return st;
+  if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  const mla::MhaPlan p = mla::make_mha_plan(dims->batch, dims->n_heads, n_q, n_k, 160, true);
+  if ((st = check_mha_workspace(p, workspace, workspace_bytes))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  mla::MhaQueryArgs qa{};
+  qa.q = q; qa.q_r = q_r; qa.q_pos = q_pos; qa.rope = rope_of(dims);
+  qa.workspace = workspace;
+  if ((st = finish(mla::launch_mha_prep_q(p, qa, s), s, "mla_chunk_attend_expanded"))) return st;
+  mla::MhaUpliftArgs ua{};
+  ua.cache = cache; ua.cap = cache_capacity; ua.d_c = dims->d_c; ua.w_uk = w_uk; ua.w_uv = w_uv; ua.workspace = workspace;
+  if ((st = finish(mla::launch_mha_uplift(p, ua, s), s, "mla_chunk_attend_expanded"))) return st;
+  const char* ws = (const char*)workspace;
+  return do_mha_attend(p, ws + p.off_k, ws + p.off_v, n_k, softmax_scale, out_dtype, out, workspace, s,
+                       "mla_chunk_attend_expanded");
+}
 
 int32_t mla_cache_append(const mla_dims* dims, int32_t dtype, const void* x, int32_t d_model, int32_t n_new,
                          const void* w_dkv, const void* w_kr, const int32_t* pos_thw, void* cache,

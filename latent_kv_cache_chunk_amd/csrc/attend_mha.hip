@@ -1,0 +1,567 @@
+// Standard multi-head attention over per-head keys and values.
+//
+// Two uses, both for comparison with the latent path of attend.hip:
+//  * the dense per-head K/V cache that VideoMLA replaces (2 x H x d_h values
+//    per token against d_c + d_r; atlas.scime.ai summary, "Key results"):
+//      out[b,i,h] = sum_j softmax_j(scale * q[b,i,h] . k[b,j,h]) v[b,j,h];
+//  * the non-absorbed form of multi-head latent attention (DeepSeek-V2,
+//    listed under "Builds on" on the VideoMLA pages): K_h = [C W_UK[h]^T || K_R]
+//    and V_h = C W_UV[h]^T are materialised from the latent cache once per
+//    call, then the same attention runs with d_qk = d_h + d_r.
+//
+// The attention kernel has the wavefront roles of attend.hip (see there):
+// a workgroup owns 256 rows of one (batch, head), in four groups of 64 with
+// a score wavefront (q in registers, S^T = K q^T by bf16 32x32x16 MFMA,
+// p = 2^(s - m), P to LDS) and a value wavefront (O^T += V^T P^T, V^T read
+// transposed from LDS) on each SIMD.  Per-head rows [k || v] are staged by
+// direct-to-LDS loads in 32-key tiles (three buffers: scored, multiplied,
+// loading); a key row is d_qk + d_v values, so 64-key tiles would not fit
+// the LDS three times over.  Partial softmax states per (workgroup, row
+// block) are merged by mha_merge_kernel.
+#include "mla_common.h"
+#include "mla_kernels.h"
+
+namespace mla {
+namespace mha {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ inline void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0), others free
+
+constexpr int kWaves = 8;          // wavefronts per workgroup
+constexpr int kGroups = 4;         // row groups (score + value wavefront each)
+constexpr int kGroupRows = 64;     // rows per group: two 32-row MFMA blocks
+constexpr int kBN = 32;            // keys per tile
+constexpr int kDV = 128;           // value width (head_dim)
+
+template <int DQK>
+struct Tile {
+  static constexpr int NK = DQK / 8;          // 16-byte chunks of a key row
+  static constexpr int NV = kDV / 8;          // 16-byte chunks of a value row
+  static constexpr int NCH = NK + NV;         // chunks of the staged [k || v] row
+  static constexpr int NSLOT = NCH + 1;       // plus one pad slot (odd stride in 16-byte units)
+  static constexpr int ROWB = NSLOT * 16;     // LDS bytes per key
+  static constexpr int TILEB = kBN * ROWB;    // LDS bytes per tile buffer
+  static constexpr int LPW = kBN / kWaves;    // one row per 64-lane load; loads per wavefront per tile
+  static constexpr int KS = DQK / 16;         // score k-steps
+  static constexpr int CB = kDV / 32;         // 32-column blocks of O^T
+  static constexpr int PBUF = kGroups * 2 * 2 * 64 * 16;   // P bytes of one tile
+  static_assert(NSLOT <= 64 && (NSLOT & 1), "a staged row fits one load, odd slot stride");
+  static_assert(3 * TILEB + 2 * PBUF <= 160 * 1024, "buffers exceed LDS");
+};
+
+struct Ctx {
+  const char* src;       // key 0 of this (batch, head) in K or V, per lane
+  uint32_t row_bytes;    // bytes between consecutive keys of the lane's tensor
+  uint32_t lane_src;     // byte offset of the lane's chunk inside its k or v row
+  bool lane_v, lane_on;  // chunk comes from V; lane copies a chunk at all
+  int n_k;
+  int wave, lane, half, group;
+  int s_off, v_off;      // LDS operand offsets inside a tile
+};
+
+// Enqueue this wavefront's direct-to-LDS loads of tile t: load i copies key
+// row (wave + kWaves * i); lane l writes slot l of that staged row (the pad
+// slot re-reads the last value chunk).  Keys past n_k re-read key n_k - 1.
+// Offsets are 32-bit: one (batch, head)'s keys span less than 4 GiB.
+template <int DQK>
+__device__ inline void issue_tile(const Ctx& c, int t, char* tile) {
+  using L = Tile<DQK>;
+#pragma unroll
+  for (int i = 0; i < L::LPW; ++i) {
+    const int row = c.wave + kWaves * i;
+    const uint32_t key = (uint32_t)min(t * kBN + row, c.n_k - 1);
+    if (c.lane_on)
+      __builtin_amdgcn_global_load_lds(c.src + (key * c.row_bytes + c.lane_src), (lds_void*)(tile + row * L::ROWB),
+                                       16, 0, 0);
+  }
+}
+
+enum class Pass { kSingle, kMax, kAccum };
+
+__device__ __forceinline__ int p_slot(int g, int qb, int part, int lane) {
+  return (((g * 2 + qb) * 2 + part) * 64 + lane) * 16;
+}
+
+__device__ __forceinline__ void mask_block(f32x16& s, int n_valid, int half) {
+  const int thr = n_valid - half * 4;
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    if ((v >> 2) * 8 + (v & 3) >= thr) s[v] = -INFINITY;
+}
+
+__device__ __forceinline__ float block_max(const f32x16& s) {
+  const float a = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  const float b = fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]));
+  const float c = fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11]));
+  const float d = fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]));
+  const float m = fmaxf(fmaxf(a, b), fmaxf(c, d));
+  return fmaxf(m, __shfl_xor(m, 32));
+}
+
+template <int DQK>
+struct ScoreState {
+  bf16x8 qf[2][Tile<DQK>::KS];
+  float qscale;          // softmax_scale * log2(e), applied to the fp32 scores
+  float m_ref[2];        // reference max, scaled (log2 units)
+  float l_run[2];
+};
+
+template <int DQK, Pass P>
+__device__ __forceinline__ void score_tile(ScoreState<DQK>& st, const char* tile, char* pbuf, int t, bool first,
+                                           const Ctx& c) {
+  using L = Tile<DQK>;
+  constexpr int KS = L::KS, PF = 4;
+  const char* kbase = tile + c.s_off;
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+  bf16x8 a[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) a[i] = *reinterpret_cast<const bf16x8*>(kbase + i * 32);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 cur = a[ks % PF];
+    if (ks + PF < KS) a[ks % PF] = *reinterpret_cast<const bf16x8*>(kbase + (ks + PF) * 32);
+    s[0] = mfma_32x32x16(cur, st.qf[0][ks], s[0]);
+    s[1] = mfma_32x32x16(cur, st.qf[1][ks], s[1]);
+  }
+  const int left = c.n_k - t * kBN;
+  if (left < 32) {
+    mask_block(s[0], left, c.half);
+    mask_block(s[1], left, c.half);
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    if (P == Pass::kMax) {
+      st.m_ref[qb] = fmaxf(st.m_ref[qb], block_max(s[qb]) * st.qscale);
+      continue;
+    }
+    if (P == Pass::kSingle && first) st.m_ref[qb] = block_max(s[qb]) * st.qscale;
+    const float m = st.m_ref[qb];
+    float p[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(s[qb][v], st.qscale, -m));
+    float q[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) q[v] = p[2 * v] + p[2 * v + 1];
+    st.l_run[qb] += ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+      bf16x8 pv;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 two = to_bf16x2(p[part * 8 + e], p[part * 8 + e + 1]);
+        pv[e] = two[0];
+        pv[e + 1] = two[1];
+      }
+      *reinterpret_cast<bf16x8*>(pbuf + p_slot(c.group, qb, part, c.lane)) = pv;
+    }
+  }
+}
+
+struct ValueState {
+  f32x16 oacc[2][kDV / 32];
+};
+
+template <int DQK>
+__device__ __forceinline__ void value_tile(ValueState& st, const char* tile, const char* pbuf, const Ctx& c) {
+  using L = Tile<DQK>;
+  const char* blk = tile + c.v_off;
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+    const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(pbuf + p_slot(c.group, 0, part, c.lane));
+    const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(pbuf + p_slot(c.group, 1, part, c.lane));
+    const char* vbase = blk + part * 16 * L::ROWB;
+#pragma unroll
+    for (int cb = 0; cb < L::CB; ++cb) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + cb * 64));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + 8 * L::ROWB + cb * 64));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      st.oacc[0][cb] = mfma_32x32x16(a, p0, st.oacc[0][cb]);
+      st.oacc[1][cb] = mfma_32x32x16(a, p1, st.oacc[1][cb]);
+    }
+  }
+}
+
+// One step: start tile k+1 into `nxt`; score tile k (`cur`, P to P[k % 2])
+// or multiply tile k-1 (`prv`, P from P[(k-1) % 2]); wait; barrier.  Steps
+// k = 0 .. n; returns true after step n.
+template <int DQK, Pass P, bool SCORE, class State>
+__device__ __forceinline__ bool sweep_step(State& st, int k, int n, int t0, char* cur, char* nxt, char* prv,
+                                           char* pb0, char* pb1, const Ctx& c) {
+  if (k + 1 < n) issue_tile<DQK>(c, t0 + k + 1, nxt);
+  if constexpr (SCORE) {
+    if (k < n) score_tile<DQK, P>(st, cur, (k & 1) ? pb1 : pb0, t0 + k, k == 0, c);
+  } else {
+    if (P != Pass::kMax && k >= 1) value_tile<DQK>(st, prv, (k & 1) ? pb0 : pb1, c);
+  }
+  wait_vmcnt0();
+  __syncthreads();
+  return k >= n;
+}
+
+template <int DQK, Pass P, bool SCORE, class State>
+__device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* k2, char* pb0, char* pb1, int t0, int t1,
+                                      const Ctx& c) {
+  const int n = t1 - t0;
+  issue_tile<DQK>(c, t0, k0);
+  wait_vmcnt0();
+  __syncthreads();
+#pragma unroll 1
+  for (int k = 0;; k += 3) {
+    if (sweep_step<DQK, P, SCORE>(st, k, n, t0, k0, k1, k2, pb0, pb1, c)) break;
+    if (sweep_step<DQK, P, SCORE>(st, k + 1, n, t0, k1, k2, k0, pb0, pb1, c)) break;
+    if (sweep_step<DQK, P, SCORE>(st, k + 2, n, t0, k2, k0, k1, pb0, pb1, c)) break;
+  }
+}
+
+struct Problem {
+  const u16* q;          // absorbed/scaled queries [B*H][rows_pad_h][DQK]
+  const u16* k;          // [B, cap, H, DQK]
+  const u16* v;          // [B, cap, H, kDV]
+  int64_t cap;
+  int H, n_k, rows_pad_h, rb_per_bh, T;
+  int64_t U;
+  int G;
+  float headroom;
+  float qscale;          // softmax_scale * log2(e)
+  float* part_L;         // [slots][256][kDV]
+  float* part_ml;        // [slots][256][2]
+};
+
+// Row block rb = (b*H + h) * rb_per_bh + rbl; units rb*T .. rb*T + T - 1.
+template <int DQK>
+__device__ __forceinline__ void begin_segment(Ctx& c, const Problem& pr, int64_t rb) {
+  const int64_t bh = rb / pr.rb_per_bh;
+  const int b = (int)(bh / pr.H), h = (int)(bh - (int64_t)b * pr.H);
+  const int64_t tok0 = (int64_t)b * pr.cap * pr.H + h;
+  c.src = c.lane_v ? reinterpret_cast<const char*>(pr.v + tok0 * kDV)
+                   : reinterpret_cast<const char*>(pr.k + tok0 * DQK);
+}
+
+template <int DQK, bool SCORE>
+__device__ __forceinline__ void role(Ctx& c, const Problem& pr, int64_t w, char* k0, char* k1, char* k2, char* pb0,
+                                     char* pb1) {
+  using L = Tile<DQK>;
+  int64_t u = unit_begin(w, pr.U, pr.G);
+  const int64_t u_end = unit_begin(w + 1, pr.U, pr.G);
+  ScoreState<DQK> ss;
+  ValueState vs;
+  while (u < u_end) {
+    const int64_t rb = u / pr.T;
+    const int t0 = (int)(u - rb * pr.T);
+    const int t1 = (int)min<int64_t>(pr.T, (int64_t)t0 + (u_end - u));
+    begin_segment<DQK>(c, pr, rb);
+    const int64_t bh = rb / pr.rb_per_bh;
+    const int rbl = (int)(rb - bh * pr.rb_per_bh);
+    bool bad = false;
+    if constexpr (SCORE) {
+      const u16* qg = pr.q + (bh * pr.rows_pad_h + (int64_t)rbl * kRowsPerBlock + c.group * kGroupRows) * DQK;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const u16* qrow = qg + (int64_t)(qb * 32 + (c.lane & 31)) * DQK + c.half * 8;
+#pragma unroll
+        for (int ks = 0; ks < L::KS; ++ks) ss.qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
+        ss.l_run[qb] = 0.f;
+        ss.m_ref[qb] = -INFINITY;
+      }
+      ss.qscale = pr.qscale;
+      sweep<DQK, Pass::kSingle, true>(ss, k0, k1, k2, pb0, pb1, t0, t1, c);
+      const float lim = __builtin_amdgcn_exp2f(pr.headroom);
+      bad = !(ss.l_run[0] <= lim) || !(ss.l_run[1] <= lim);
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int cb = 0; cb < L::CB; ++cb) vs.oacc[qb][cb] = f32x16{};
+      sweep<DQK, Pass::kSingle, false>(vs, k0, k1, k2, pb0, pb1, t0, t1, c);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int cb = 0; cb < L::CB; ++cb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) bad |= !(fabsf(vs.oacc[qb][cb][v]) <= 3.0e38f);
+    }
+    if (__syncthreads_or(bad)) {
+      // exact two-pass evaluation of this segment: the true max, then accumulation
+      if constexpr (SCORE) {
+        ss.m_ref[0] = ss.m_ref[1] = -INFINITY;
+        sweep<DQK, Pass::kMax, true>(ss, k0, k1, k2, pb0, pb1, t0, t1, c);
+        ss.l_run[0] = ss.l_run[1] = 0.f;
+        sweep<DQK, Pass::kAccum, true>(ss, k0, k1, k2, pb0, pb1, t0, t1, c);
+      } else {
+        sweep<DQK, Pass::kMax, false>(vs, k0, k1, k2, pb0, pb1, t0, t1, c);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int cb = 0; cb < L::CB; ++cb) vs.oacc[qb][cb] = f32x16{};
+        sweep<DQK, Pass::kAccum, false>(vs, k0, k1, k2, pb0, pb1, t0, t1, c);
+      }
+    }
+    const int64_t slot = seg_slot(w, rb);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int rl = c.group * kGroupRows + qb * 32 + (c.lane & 31);
+      if constexpr (SCORE) {
+        const float l_tot = ss.l_run[qb] + __shfl_xor(ss.l_run[qb], 32);
+        if (c.half == 0) {
+          pr.part_ml[(slot * kRowsPerBlock + rl) * 2 + 0] = ss.m_ref[qb];
+          pr.part_ml[(slot * kRowsPerBlock + rl) * 2 + 1] = l_tot;
+        }
+      } else {
+        float* Ld = pr.part_L + (slot * kRowsPerBlock + rl) * kDV;
+#pragma unroll
+        for (int cb = 0; cb < L::CB; ++cb)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            const int c0 = cb * 32 + gg * 8 + c.half * 4;
+            *reinterpret_cast<f32x4*>(Ld + c0) = f32x4{vs.oacc[qb][cb][4 * gg], vs.oacc[qb][cb][4 * gg + 1],
+                                                       vs.oacc[qb][cb][4 * gg + 2], vs.oacc[qb][cb][4 * gg + 3]};
+          }
+      }
+    }
+    u += (t1 - t0);
+  }
+}
+
+template <int DQK>
+__global__ __launch_bounds__(kWaves * 64, 1)
+void mha_attend_kernel(Problem pr) {
+  using L = Tile<DQK>;
+  __shared__ __attribute__((aligned(1024))) char kbuf0[L::TILEB];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[L::TILEB];
+  __shared__ __attribute__((aligned(1024))) char kbuf2[L::TILEB];
+  __shared__ __attribute__((aligned(1024))) char pbuf0[L::PBUF];
+  __shared__ __attribute__((aligned(1024))) char pbuf1[L::PBUF];
+  Ctx c;
+  c.n_k = pr.n_k;
+  c.lane = threadIdx.x & 63;
+  c.half = c.lane >> 5;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool scorer = c.wave < kGroups;   // wavefronts w and w + 4 share a SIMD
+  c.group = c.wave & (kGroups - 1);
+  const int ch = min(c.lane, L::NCH - 1);  // the pad lane re-copies the last chunk
+  c.lane_on = c.lane < L::NSLOT;
+  c.lane_v = ch >= L::NK;
+  c.lane_src = (uint32_t)((c.lane_v ? ch - L::NK : ch) * 16);
+  c.row_bytes = (uint32_t)pr.H * (c.lane_v ? kDV : DQK) * 2;
+  c.s_off = (c.lane & 31) * L::ROWB + c.half * 16;
+  const int g = c.lane >> 4, j = c.lane & 15;
+  c.v_off = ((g >> 1) * 4 + (j >> 2)) * L::ROWB + (16 * (g & 1) + 4 * (j & 3)) * 2 + DQK * 2;
+  const int64_t w = (int64_t)pr.G - 1 - blockIdx.x;
+  if (scorer) role<DQK, true>(c, pr, w, kbuf0, kbuf1, kbuf2, pbuf0, pbuf1);
+  else role<DQK, false>(c, pr, w, kbuf0, kbuf1, kbuf2, pbuf0, pbuf1);
+}
+
+// out[b, i, h, :] = sum_s 2^(m_s - M) L_s / sum_s 2^(m_s - M) l_s over the
+// partial states of row (b, h, i).  16 threads per row, 8 columns each.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256)
+void mha_merge_kernel(const float* __restrict__ part_L, const float* __restrict__ part_ml, int B, int H, int n_q,
+                      int rb_per_bh, int T, int64_t U, int G, void* __restrict__ out) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  if (row >= (int64_t)B * n_q * H) return;
+  const int h = (int)(row % H);
+  const int64_t bi = row / H;
+  const int i = (int)(bi % n_q), b = (int)(bi / n_q);
+  const int64_t rb = ((int64_t)b * H + h) * rb_per_bh + i / kRowsPerBlock;
+  const int rl = i % kRowsPerBlock;
+  const int64_t wa = unit_owner(rb * T, U, G), wb = unit_owner(rb * T + T - 1, U, G);
+  float M = -INFINITY;
+  for (int64_t w = wa; w <= wb; ++w) M = fmaxf(M, part_ml[(seg_slot(w, rb) * kRowsPerBlock + rl) * 2]);
+  float l = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int64_t w = wa; w <= wb; ++w) {
+    const int64_t sl = seg_slot(w, rb);
+    const float wt = exp2f(part_ml[(sl * kRowsPerBlock + rl) * 2] - M);
+    l = fmaf(wt, part_ml[(sl * kRowsPerBlock + rl) * 2 + 1], l);
+    const f32x4* src = reinterpret_cast<const f32x4*>(part_L + (sl * kRowsPerBlock + rl) * kDV + sub * 8);
+    const f32x4 x0 = src[0], x1 = src[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] = fmaf(wt, x0[e], acc[e]);
+      acc[4 + e] = fmaf(wt, x1[e], acc[4 + e]);
+    }
+  }
+  const float inv = 1.f / l;
+  const int64_t o = row * kDV + sub * 8;
+  if (OUT_F32) {
+    f32x4* dst = reinterpret_cast<f32x4*>((float*)out + o);
+    dst[0] = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    dst[1] = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+  } else {
+    uint32_t wds[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wds[e] = bf16x2_bits(to_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv));
+    *reinterpret_cast<uint4*>((u16*)out + o) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+  }
+}
+
+// Queries in the attention kernel's layout: qt[(b*H + h)][i][e] =
+// bf16(qfull[b, i, h, e]) with qfull = q (dense: an exact copy) or
+// [q_h || RoPE3D(p_i) q_r,h] (non-absorbed latent); rows past n_q are zero.
+// The softmax scale is applied to the fp32 scores, so no query is rounded
+// after scaling.  One thread per (row, element pair).
+__global__ __launch_bounds__(256)
+void mha_prep_q_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r, const int* __restrict__ q_pos,
+                       int B, int H, int n_q, int dh, int dr, int rows_pad_h, RopeSpec rope,
+                       u16* __restrict__ qt) {
+  const int dqk = dh + dr, pairs = dqk / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)B * H * rows_pad_h * pairs;
+  if (idx >= total) return;
+  const int pr = (int)(idx % pairs);
+  const int64_t rowg = idx / pairs;              // (b*H + h) * rows_pad_h + i
+  const int i = (int)(rowg % rows_pad_h);
+  const int64_t bh = rowg / rows_pad_h;
+  const int h = (int)(bh % H), b = (int)(bh / H);
+  float x0 = 0.f, x1 = 0.f;
+  if (i < n_q) {
+    const int e = 2 * pr;
+    if (e < dh) {
+      const u16* src = q + (((int64_t)b * n_q + i) * H + h) * dh + e;
+      x0 = (float)__builtin_bit_cast(__bf16, src[0]);
+      x1 = (float)__builtin_bit_cast(__bf16, src[1]);
+    } else {
+      const int er = e - dh;
+      const u16* src = q_r + (((int64_t)b * n_q + i) * H + h) * dr + er;
+      const float a = (float)__builtin_bit_cast(__bf16, src[0]), c = (float)__builtin_bit_cast(__bf16, src[1]);
+      const double ang = rope_angle(er >> 1, q_pos[3 * i], q_pos[3 * i + 1], q_pos[3 * i + 2], rope);
+      const float cs = (float)cos(ang), sn = (float)sin(ang);
+      x0 = fmaf(a, cs, -(c * sn));
+      x1 = fmaf(a, sn, c * cs);
+    }
+  }
+  *reinterpret_cast<uint32_t*>(qt + rowg * dqk + 2 * pr) = bf16x2_bits(to_bf16x2(x0, x1));
+}
+
+// Per-head keys and values from the latent cache (non-absorbed form):
+//   K[b, j, h, 0:dh]   = W_UK[h] c_j,   K[b, j, h, dh:dh+dr] = k_R,j
+//   V[b, j, h, :]      = W_UV[h] c_j
+// Workgroup (32 tokens, one head, K or V) with 4 wavefronts of 32 outputs:
+// C^T[o][token] = sum_k W[o][k] c[token][k] by bf16 MFMA 32x32x16, fp32
+// accumulation, one rounding to bf16.  The K workgroup also copies k_R.
+template <int DC>
+__global__ __launch_bounds__(256)
+void mha_uplift_kernel(const u16* __restrict__ cache, int64_t cap, int n_k, int ntok, int H,
+                       const u16* __restrict__ w_uk, const u16* __restrict__ w_uv,
+                       u16* __restrict__ K, u16* __restrict__ V) {
+  constexpr int W = DC + 32, DH = 128, DQK = DH + 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+  const int tok0 = blockIdx.x * 32;
+  const int h = blockIdx.y >> 1;
+  const bool is_v = blockIdx.y & 1;
+  const int my_tok = min(tok0 + (lane & 31), ntok - 1);
+  const int b = my_tok / n_k, j = my_tok - b * n_k;
+  const u16* crow = cache + ((int64_t)b * cap + j) * W + half * 8;
+  const int o = wave * 32 + (lane & 31);
+  const u16* wrow = (is_v ? w_uv : w_uk) + ((int64_t)h * DH + o) * DC + half * 8;
+  f32x16 acc = {};
+#pragma unroll
+  for (int k = 0; k < DC / 16; ++k)
+    acc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(wrow + k * 16), *reinterpret_cast<const bf16x8*>(crow + k * 16),
+                        acc);
+  // lane holds token (lane & 31), outputs wave*32 + 8g + 4*half + t
+  const int tok = tok0 + (lane & 31);
+  if (tok < ntok) {
+    const int tb = tok / n_k, tj = tok - tb * n_k;
+    const int64_t kv_row = ((int64_t)tb * n_k + tj) * H + h;   // K and V hold exactly n_k keys per sample
+    u16* dst = is_v ? V + kv_row * DH : K + kv_row * DQK;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int o0 = wave * 32 + gq * 8 + half * 4;
+      *reinterpret_cast<uint2*>(dst + o0) = make_uint2(bf16x2_bits(to_bf16x2(acc[4 * gq], acc[4 * gq + 1])),
+                                                       bf16x2_bits(to_bf16x2(acc[4 * gq + 2], acc[4 * gq + 3])));
+    }
+    if (!is_v && wave == 0) {   // the positional key, shared by every head
+      const u16* kr = cache + ((int64_t)tb * cap + tj) * W + DC + half * 16;
+      *reinterpret_cast<uint4*>(dst + DH + half * 16) = *reinterpret_cast<const uint4*>(kr);
+      *reinterpret_cast<uint4*>(dst + DH + half * 16 + 8) = *reinterpret_cast<const uint4*>(kr + 8);
+    }
+  }
+}
+
+}  // namespace mha
+
+// ----------------------------------------------------------------- plans
+MhaPlan make_mha_plan(int B, int H, int n_q, int n_k, int dqk, bool expanded) {
+  MhaPlan p{};
+  p.B = B; p.H = H; p.n_q = n_q; p.n_k = n_k; p.dqk = dqk;
+  p.rb_per_bh = (n_q + kRowsPerBlock - 1) / kRowsPerBlock;
+  p.rows_pad_h = p.rb_per_bh * kRowsPerBlock;
+  p.nrb = (int64_t)B * H * p.rb_per_bh;
+  p.T = (n_k + mha::kBN - 1) / mha::kBN;
+  p.U = p.nrb * p.T;
+  int64_t G = p.nrb;
+  const int64_t rounds = (p.nrb + kPartitionCUs - 1) / kPartitionCUs;
+  if ((double)p.nrb / (double)(rounds * kPartitionCUs) < 0.9) G = rounds * kPartitionCUs;
+  if (G > p.U) G = p.U;
+  p.G = (int32_t)G;
+  const int64_t slots = G + p.nrb;
+  p.off_qt = 0;
+  p.off_L = align_up((int64_t)B * H * p.rows_pad_h * dqk * 2, 256);
+  p.off_ml = align_up(p.off_L + slots * kRowsPerBlock * mha::kDV * 4, 256);
+  p.off_k = align_up(p.off_ml + slots * kRowsPerBlock * 2 * 4, 256);
+  p.off_v = p.off_k;
+  p.total = p.off_k;
+  if (expanded) {   // materialised per-head K [B, n_k, H, dqk] and V [B, n_k, H, 128]
+    p.off_v = align_up(p.off_k + (int64_t)B * n_k * H * dqk * 2, 256);
+    p.total = align_up(p.off_v + (int64_t)B * n_k * H * mha::kDV * 2, 256);
+  }
+  return p;
+}
+
+hipError_t launch_mha_prep_q(const MhaPlan& p, const MhaQueryArgs& a, hipStream_t s) {
+  const int64_t work = (int64_t)p.B * p.H * p.rows_pad_h * (p.dqk / 2);
+  mha::mha_prep_q_kernel<<<dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s>>>(
+      (const u16*)a.q, (const u16*)a.q_r, a.q_pos, p.B, p.H, p.n_q, 128, p.dqk - 128, p.rows_pad_h, a.rope,
+      (u16*)((char*)a.workspace + p.off_qt));
+  return hipGetLastError();
+}
+
+hipError_t launch_mha_uplift(const MhaPlan& p, const MhaUpliftArgs& a, hipStream_t s) {
+  char* ws = (char*)a.workspace;
+  const int ntok = p.B * p.n_k;
+  const dim3 grid((ntok + 31) / 32, 2 * p.H), block(256);
+  u16* K = (u16*)(ws + p.off_k);
+  u16* V = (u16*)(ws + p.off_v);
+  switch (a.d_c) {
+    case 64: mha::mha_uplift_kernel<64><<<grid, block, 0, s>>>((const u16*)a.cache, a.cap, p.n_k, ntok, p.H, (const u16*)a.w_uk, (const u16*)a.w_uv, K, V); break;
+    case 128: mha::mha_uplift_kernel<128><<<grid, block, 0, s>>>((const u16*)a.cache, a.cap, p.n_k, ntok, p.H, (const u16*)a.w_uk, (const u16*)a.w_uv, K, V); break;
+    case 192: mha::mha_uplift_kernel<192><<<grid, block, 0, s>>>((const u16*)a.cache, a.cap, p.n_k, ntok, p.H, (const u16*)a.w_uk, (const u16*)a.w_uv, K, V); break;
+    case 256: mha::mha_uplift_kernel<256><<<grid, block, 0, s>>>((const u16*)a.cache, a.cap, p.n_k, ntok, p.H, (const u16*)a.w_uk, (const u16*)a.w_uv, K, V); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mha_attend(const MhaPlan& p, const MhaAttendArgs& a, hipStream_t s) {
+  char* ws = (char*)a.workspace;
+  mha::Problem pr{};
+  pr.q = (const u16*)(ws + p.off_qt);
+  pr.k = (const u16*)a.k;
+  pr.v = (const u16*)a.v;
+  pr.cap = a.cap;
+  pr.H = p.H; pr.n_k = p.n_k; pr.rows_pad_h = p.rows_pad_h; pr.rb_per_bh = p.rb_per_bh; pr.T = p.T;
+  pr.U = p.U; pr.G = p.G; pr.headroom = a.headroom; pr.qscale = a.qscale;
+  pr.part_L = (float*)(ws + p.off_L);
+  pr.part_ml = (float*)(ws + p.off_ml);
+  switch (p.dqk) {
+    case 128: mha::mha_attend_kernel<128><<<dim3(p.G), dim3(mha::kWaves * 64), 0, s>>>(pr); break;
+    case 160: mha::mha_attend_kernel<160><<<dim3(p.G), dim3(mha::kWaves * 64), 0, s>>>(pr); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  const int64_t rows = (int64_t)p.B * p.n_q * p.H;
+  const dim3 grid((unsigned)((rows + 15) / 16)), block(256);
+  if (a.out_f32)
+    mha::mha_merge_kernel<true><<<grid, block, 0, s>>>(pr.part_L, pr.part_ml, p.B, p.H, p.n_q, p.rb_per_bh, p.T, p.U,
+                                                       p.G, a.out);
+  else
+    mha::mha_merge_kernel<false><<<grid, block, 0, s>>>(pr.part_L, pr.part_ml, p.B, p.H, p.n_q, p.rb_per_bh, p.T,
+                                                        p.U, p.G, a.out);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -40,6 +40,58 @@ struct UpprojArgs {
   void* workspace;
 };
 
+// ---------------------------------------------------------------------------
+// Standard attention over per-head keys and values (attend_mha.hip): the
+// dense K/V baseline and the non-absorbed latent form.  bf16 inputs, head_dim
+// and value width 128, query/key width dqk = 128 (dense) or 160 (latent:
+// d_h + d_r).  Rows are padded per (batch, head) to 256-row blocks.
+// ---------------------------------------------------------------------------
+struct MhaPlan {
+  int32_t B, H, n_q, n_k, dqk;
+  int32_t rb_per_bh, rows_pad_h;   // row blocks and padded rows per (batch, head)
+  int64_t nrb;                     // B * H * rb_per_bh
+  int32_t T;                       // 32-key tiles
+  int64_t U;                       // units nrb * T
+  int32_t G;                       // attention workgroups
+  // byte offsets inside the workspace: scaled queries, partial states,
+  // and (non-absorbed form) the materialised per-head K and V
+  int64_t off_qt, off_L, off_ml, off_k, off_v, total;
+};
+
+MhaPlan make_mha_plan(int B, int H, int n_q, int n_k, int dqk, bool expanded);
+
+struct MhaQueryArgs {
+  const void* q;        // [B, n_q, H, 128]
+  const void* q_r;      // [B, n_q, H, dqk - 128] (dqk = 160), else unused
+  const int* q_pos;     // [n_q, 3] (dqk = 160), else unused
+  RopeSpec rope;
+  void* workspace;
+};
+
+struct MhaUpliftArgs {
+  const void* cache;    // [B, cap, d_c + 32]
+  int64_t cap;
+  int d_c;
+  const void* w_uk;     // [H, 128, d_c]
+  const void* w_uv;     // [H, 128, d_c]
+  void* workspace;
+};
+
+struct MhaAttendArgs {
+  const void* k;        // [B, cap, H, dqk]
+  const void* v;        // [B, cap, H, 128]
+  int64_t cap;
+  float headroom;
+  float qscale;         // softmax_scale * log2(e), applied to the fp32 scores
+  void* out;            // [B, n_q, H, 128]
+  bool out_f32;
+  void* workspace;
+};
+
+hipError_t launch_mha_prep_q(const MhaPlan& p, const MhaQueryArgs& a, hipStream_t s);
+hipError_t launch_mha_uplift(const MhaPlan& p, const MhaUpliftArgs& a, hipStream_t s);
+hipError_t launch_mha_attend(const MhaPlan& p, const MhaAttendArgs& a, hipStream_t s);
+
 hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s);
 hipError_t launch_append_f32(const AppendArgs& a, hipStream_t s);
 hipError_t launch_absorb_bf16(const Plan& p, const AbsorbArgs& a, hipStream_t s);

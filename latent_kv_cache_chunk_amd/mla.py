@@ -29,7 +29,9 @@ EXPORTED = ("mla_cache_append", "mla_chunk_attend_workspace_bytes", "mla_chunk_a
             "mla_chunk_attend_causal", "mla_query_absorb", "mla_latent_attend", "mla_latent_attend_causal",
             "mla_value_upproj", "mla_status_string", "mla_last_error", "mla_version",
             "mla_ring_init", "mla_ring_current", "mla_ring_commit", "mla_ring_slot_chunks",
-            "mla_cache_bytes", "mla_dense_kv_bytes", "mla_ring_last_error")
+            "mla_cache_bytes", "mla_dense_kv_bytes", "mla_ring_last_error",
+            "mla_mha_attend_workspace_bytes", "mla_mha_attend",
+            "mla_chunk_attend_expanded_workspace_bytes", "mla_chunk_attend_expanded")
 
 
 class MlaDims(ctypes.Structure):
@@ -72,6 +74,17 @@ _lib.mla_latent_attend_causal.restype = _I32
 _lib.mla_value_upproj.argtypes = [_DIMS, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P]
 _lib.mla_value_upproj.restype = _I32
 _RING = ctypes.POINTER(MlaRing)
+_lib.mla_mha_attend_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
+_lib.mla_mha_attend_workspace_bytes.restype = _I64
+_lib.mla_mha_attend.argtypes = [_I32, _I32, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, ctypes.c_float, _P, _P, _I64,
+                                _P]
+_lib.mla_mha_attend.restype = _I32
+_lib.mla_chunk_attend_expanded_workspace_bytes.argtypes = [_DIMS, _I32, _I32]
+_lib.mla_chunk_attend_expanded_workspace_bytes.restype = _I64
+_lib.mla_chunk_attend_expanded.argtypes = [_DIMS, _I32, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, ctypes.c_float,
+                                           _P, _P, _I64, _P]
+_lib.mla_chunk_attend_expanded.restype = _I32
+
 _lib.mla_ring_init.argtypes = [_RING, _I32, _I32, _I32]
 _lib.mla_ring_init.restype = _I32
 _lib.mla_ring_current.argtypes = [_RING, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]
@@ -254,6 +267,66 @@ def value_upproj(dims: Dims, w_uv, out, n_q: int, n_k: int, workspace, stream=No
                                  int(n_k), w_uv.data_ptr(), out.data_ptr(), workspace.data_ptr(),
                                  workspace.numel(), _stream(stream))
     _raise(code, "mla_value_upproj")
+
+
+def mha_workspace_bytes(batch: int, n_heads: int, head_dim: int, n_q: int, n_k: int) -> int:
+    n = _lib.mla_mha_attend_workspace_bytes(int(batch), int(n_heads), int(head_dim), int(n_q), int(n_k))
+    if n < 0:
+        _raise(int(n), "mla_mha_attend_workspace_bytes")
+    return int(n)
+
+
+def mha_attend(q, k, v, n_k: int, scale: float, out=None, out_dtype=None, workspace=None,
+               stream=None) -> torch.Tensor:
+    """Dense per-head attention (mla_mha_attend): out[b,i,h] = softmax_j(scale q.k_j) v_j, j < n_k.
+
+    q [B, n_q, H, d_h]; k, v [B, capacity, H, d_h]; bf16."""
+    B, n_q, H, dh = q.shape
+    cap = k.shape[1]
+    _check(q, "q", (B, n_q, H, dh), torch.bfloat16)
+    _check(k, "k", (B, cap, H, dh), torch.bfloat16)
+    _check(v, "v", (B, cap, H, dh), torch.bfloat16)
+    odt = torch.bfloat16 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, n_q, H, dh), dtype=odt, device=q.device)
+    _check(out, "out", (B, n_q, H, dh), odt)
+    if workspace is None:
+        workspace = torch.empty(mha_workspace_bytes(B, H, dh, n_q, n_k), dtype=torch.uint8, device=q.device)
+    code = _lib.mla_mha_attend(B, H, dh, _dtype_code(odt), q.data_ptr(), n_q, k.data_ptr(), v.data_ptr(), cap,
+                               int(n_k), float(scale), out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                               _stream(stream))
+    _raise(code, "mla_mha_attend")
+    return out
+
+
+def expanded_workspace_bytes(dims: Dims, n_q: int, n_k: int) -> int:
+    d = dims.c()
+    n = _lib.mla_chunk_attend_expanded_workspace_bytes(ctypes.byref(d), int(n_q), int(n_k))
+    if n < 0:
+        _raise(int(n), "mla_chunk_attend_expanded_workspace_bytes")
+    return int(n)
+
+
+def chunk_attend_expanded(dims: Dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k: int, scale: float,
+                          out=None, out_dtype=None, workspace=None, stream=None) -> torch.Tensor:
+    """chunk_attend in the non-absorbed form (mla_chunk_attend_expanded): per-head K_h, V_h are
+    materialised from the latent cache, then standard attention runs over them.  bf16."""
+    n_q, dt = _attend_checks(dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k)
+    if dt != torch.bfloat16:
+        raise TypeError("chunk_attend_expanded takes bfloat16 inputs")
+    odt = dt if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((dims.batch, n_q, dims.n_heads, dims.head_dim), dtype=odt, device=q.device)
+    _check(out, "out", (dims.batch, n_q, dims.n_heads, dims.head_dim), odt)
+    if workspace is None:
+        workspace = torch.empty(expanded_workspace_bytes(dims, n_q, n_k), dtype=torch.uint8, device=q.device)
+    d = dims.c()
+    code = _lib.mla_chunk_attend_expanded(ctypes.byref(d), _dtype_code(odt), q.data_ptr(), q_r.data_ptr(),
+                                          q_pos.data_ptr(), n_q, w_uk.data_ptr(), w_uv.data_ptr(), cache.data_ptr(),
+                                          cache.shape[1], int(n_k), float(scale), out.data_ptr(),
+                                          workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _raise(code, "mla_chunk_attend_expanded")
+    return out
 
 
 class Ring:

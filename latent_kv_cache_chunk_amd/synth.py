@@ -15,6 +15,7 @@ bf16 when the bf16 dtype is requested):
   attention inputs  c_KV ~ N(0, 1), k_R ~ N(0, 1), q ~ N(0, 1), q_r ~ N(0, 1),
                     W_UK, W_UV ~ N(0, 1/d_c)
   append inputs     x ~ N(0, 1), W_DKV, W_KR ~ N(0, 1/D)
+  dense K/V inputs  q, k, v ~ N(0, 1) per head (sample b: PCG64(3000 + b + 7919*seed))
   seeds             weights: PCG64(7 + 7919*seed); batch sample b:
                     PCG64(1000 + b + 7919*seed) (its own cache, q, q_r, x).
 Positions: latent token n of a chunk is frame-major then row-major,
@@ -99,7 +100,16 @@ class Workload:
         return float(self.batch * self.n_heads * self.visible_keys()) * (4 * self.d_c + 2 * self.d_r)
 
     def mha_equiv_flops(self) -> float:
+        """Flops of standard attention over materialised per-head keys [k_h || k_R] and values."""
         return float(self.batch * self.n_heads * self.visible_keys()) * (4 * self.head_dim + 2 * self.d_r)
+
+    def dense_flops(self) -> float:
+        """Flops of standard attention over a dense per-head K/V cache (d_h-wide keys and values)."""
+        return float(self.batch * self.n_heads * self.visible_keys()) * 4 * self.head_dim
+
+    def expand_flops(self) -> float:
+        """Flops of materialising K_h = W_UK[h] c and V_h = W_UV[h] c for every key."""
+        return 4.0 * self.batch * self.n_k * self.n_heads * self.head_dim * self.d_c
 
     def append_flops(self) -> float:
         return 2.0 * self.batch * self.n_q * self.d_model * (self.d_c + self.d_r)
@@ -179,6 +189,25 @@ def attend_inputs(wl: Workload, seed: int = 0, dtype: torch.dtype = torch.bfloat
         q_pos=torch.from_numpy(chunk_positions(wl.query_frames, wl.grid_hw)),
         n_k=wl.n_k, scale=wl.scale,
     )
+
+
+def mha_inputs(wl: Workload, seed: int = 0, capacity: int | None = None) -> dict:
+    """Queries and a dense per-head K/V cache [B, capacity, H, d_h] for the same
+    chunk step (the cache layout the latent replaces); bf16, every value N(0, 1),
+    scale 1/sqrt(d_h).  Slots past n_k are zero."""
+    cap = wl.n_k if capacity is None else capacity
+    assert cap >= wl.n_k
+    H, d = wl.n_heads, wl.head_dim
+    q = np.empty((wl.batch, wl.n_q, H, d), np.float32)
+    k = np.zeros((wl.batch, cap, H, d), np.float32)
+    v = np.zeros((wl.batch, cap, H, d), np.float32)
+    for b in range(wl.batch):
+        r = _rng(3000 + b + 7919 * seed)
+        q[b] = _normal(r, q.shape[1:])
+        k[b, :wl.n_k] = _normal(r, (wl.n_k, H, d))
+        v[b, :wl.n_k] = _normal(r, (wl.n_k, H, d))
+    bf = torch.bfloat16
+    return dict(q=_to(q, bf), k=_to(k, bf), v=_to(v, bf), n_k=wl.n_k, scale=1.0 / float(np.sqrt(d)))
 
 
 def append_inputs(wl: Workload, seed: int = 0, dtype: torch.dtype = torch.bfloat16) -> dict:

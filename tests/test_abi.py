@@ -156,6 +156,42 @@ def test_causal_validation():
                                         ctypes.byref(mla.MlaCausal(144, 0)), fake, 1 << 40, None) == -1
 
 
+def test_mha_validation_and_workspace():
+    lib = mla.raw()
+    fake = ctypes.c_void_p(0x10000)
+    ws_dense = lib.mla_mha_attend_workspace_bytes(1, 12, 128, 4680, 32760)
+    assert ws_dense > 0 and ws_dense % 256 == 0
+    assert lib.mla_mha_attend_workspace_bytes(1, 12, 64, 4680, 32760) == -2
+    assert lib.mla_mha_attend_workspace_bytes(1, 12, 128, 0, 32760) == -1
+    assert lib.mla_mha_attend_workspace_bytes(1, 12, 128, 100, 99) == -1
+
+    def dense(head_dim=128, q=fake, n_q=48, cap=192, n_k=192, scale=0.08, ws_bytes=1 << 40):
+        return lib.mla_mha_attend(1, 12, head_dim, 0, q, n_q, fake, fake, cap, n_k, ctypes.c_float(scale), fake,
+                                  fake, ws_bytes, None)
+
+    assert dense(head_dim=96) == -2
+    assert dense(q=None) == -1 and b"q is null" in lib.mla_last_error()
+    assert dense(cap=100) == -1 and b"cache_capacity" in lib.mla_last_error()
+    assert dense(scale=0.0) == -1
+    assert dense(ws_bytes=1024) == -3
+    assert dense(cap=(1 << 21)) == -2        # one sample's K would pass 4 GiB
+
+    d = _dims()
+    ws_exp = lib.mla_chunk_attend_expanded_workspace_bytes(ctypes.byref(d), 4680, 32760)
+    # the materialised per-head K (160 wide) and V (128 wide) dominate
+    assert ws_exp > 32760 * 12 * (160 + 128) * 2
+    bad = _dims(head_dim=64)
+    assert lib.mla_chunk_attend_expanded_workspace_bytes(ctypes.byref(bad), 48, 192) == -2
+
+    def expanded(q_pos=fake, n_k=192, cap=192, ws_bytes=1 << 40):
+        return lib.mla_chunk_attend_expanded(ctypes.byref(d), 0, fake, fake, q_pos, 48, fake, fake, fake, cap, n_k,
+                                             ctypes.c_float(0.08), fake, fake, ws_bytes, None)
+
+    assert expanded(q_pos=None) == -1 and b"q_pos" in lib.mla_last_error()
+    assert expanded(n_k=200) == -1
+    assert expanded(ws_bytes=4096) == -3
+
+
 def test_binding_checks_tensors_on_host():
     d = mla.Dims(batch=1)
     with pytest.raises(ValueError):
