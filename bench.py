@@ -93,6 +93,55 @@ def cpu_baseline(wl, inputs, n_heads: int) -> dict:
                       f"rate = absorbed algorithmic flops of the sample / wall time"}
 
 
+def _time_calls(fn, steps: int, warmup: int) -> float:
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def compare(wl, dims, t, latent_ms: float, seed: int, dev, steps: int = 20, warmup: int = 3) -> dict:
+    """The same chunk step's attention over a dense per-head K/V cache (the
+    layout the latent replaces: 2*H*d_h values per token) and in the
+    non-absorbed latent form (per-head K_h, V_h materialised from the latent,
+    then standard attention), against the absorbed path's absorb + attend +
+    up-projection time measured above.  Cache appends are excluded from all three."""
+    import torch
+    from latent_kv_cache_chunk_amd import mla, synth
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in synth.mha_inputs(wl, seed=seed).items()}
+    out = torch.empty((wl.batch, wl.n_q, wl.n_heads, wl.head_dim), dtype=torch.bfloat16, device=dev)
+    ws_d = torch.empty(mla.mha_workspace_bytes(wl.batch, wl.n_heads, wl.head_dim, wl.n_q, wl.n_k),
+                       dtype=torch.uint8, device=dev)
+    dense_ms = _time_calls(lambda: mla.mha_attend(d["q"], d["k"], d["v"], wl.n_k, d["scale"], out=out,
+                                                  workspace=ws_d), steps, warmup)
+    del d, ws_d
+    ws_e = torch.empty(mla.expanded_workspace_bytes(dims, wl.n_q, wl.n_k), dtype=torch.uint8, device=dev)
+    exp_ms = _time_calls(lambda: mla.chunk_attend_expanded(dims, t["q"], t["q_r"], t["q_pos"], t["w_uk"], t["w_uv"],
+                                                           t["cache"], wl.n_k, wl.scale, out=out, workspace=ws_e),
+                         steps, warmup)
+    del ws_e
+    lat_bytes = mla.cache_bytes(dims, torch.bfloat16, wl.n_k)
+    dense_bytes = mla.dense_kv_bytes(dims, torch.bfloat16, wl.n_k)
+    return {
+        "latent_absorbed_ms": round(latent_ms, 4),
+        "dense_mha_ms": round(dense_ms, 4),
+        "latent_expanded_ms": round(exp_ms, 4),
+        "dense_over_latent_time": round(dense_ms / latent_ms, 3),
+        "expanded_over_absorbed_time": round(exp_ms / latent_ms, 3),
+        "cache_bytes": {"latent": lat_bytes, "dense_kv": dense_bytes, "ratio": round(dense_bytes / lat_bytes, 2)},
+        "flop_per_row_key": {"absorbed": 4 * wl.d_c + 2 * wl.d_r, "expanded": 4 * wl.head_dim + 2 * wl.d_r,
+                             "dense": 4 * wl.head_dim},
+        "steps": steps,
+    }
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +151,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads whose rows form the oracle sample")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the dense per-head K/V and non-absorbed comparison timings")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for rocprofv3 --pmc runs: a plain copy of known size, then a few steps; no timing")
     args = ap.parse_args(argv)
@@ -210,6 +261,8 @@ def main(argv=None) -> int:
                                  f"({wl.batch * wl.n_q * wl.n_heads} rows, {wl.n_k} keys)"},
         "cpu_baseline": None,
     }
+    if not args.no_compare and not wl.causal:
+        res["comparison"] = compare(wl, dims, t, absorb_ms + attend_ms + upproj_ms, args.seed, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, att, args.cpu_heads)
     print(json.dumps(res))

@@ -402,83 +402,99 @@ void mha_merge_kernel(const float* __restrict__ part_L, const float* __restrict_
 // bf16(qfull[b, i, h, e]) with qfull = q (dense: an exact copy) or
 // [q_h || RoPE3D(p_i) q_r,h] (non-absorbed latent); rows past n_q are zero.
 // The softmax scale is applied to the fp32 scores, so no query is rounded
-// after scaling.  One thread per (row, element pair).
+// after scaling.  Thread = 8 consecutive elements (16 bytes) of one row;
+// grid.y = b*H + h.
 __global__ __launch_bounds__(256)
 void mha_prep_q_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r, const int* __restrict__ q_pos,
-                       int B, int H, int n_q, int dh, int dr, int rows_pad_h, RopeSpec rope,
-                       u16* __restrict__ qt) {
-  const int dqk = dh + dr, pairs = dqk / 2;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)B * H * rows_pad_h * pairs;
-  if (idx >= total) return;
-  const int pr = (int)(idx % pairs);
-  const int64_t rowg = idx / pairs;              // (b*H + h) * rows_pad_h + i
-  const int i = (int)(rowg % rows_pad_h);
-  const int64_t bh = rowg / rows_pad_h;
-  const int h = (int)(bh % H), b = (int)(bh / H);
-  float x0 = 0.f, x1 = 0.f;
+                       int H, int n_q, int dr, int rows_pad_h, RopeSpec rope, u16* __restrict__ qt) {
+  constexpr int DH = 128, NQ = DH / 8;
+  const int nch = NQ + dr / 8;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows_pad_h * nch) return;
+  const int i = idx / nch, ch = idx - i * nch;
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  uint4 val = make_uint4(0, 0, 0, 0);
   if (i < n_q) {
-    const int e = 2 * pr;
-    if (e < dh) {
-      const u16* src = q + (((int64_t)b * n_q + i) * H + h) * dh + e;
-      x0 = (float)__builtin_bit_cast(__bf16, src[0]);
-      x1 = (float)__builtin_bit_cast(__bf16, src[1]);
+    const int64_t tok = ((int64_t)b * n_q + i) * H + h;
+    if (ch < NQ) {
+      val = *reinterpret_cast<const uint4*>(q + tok * DH + ch * 8);
     } else {
-      const int er = e - dh;
-      const u16* src = q_r + (((int64_t)b * n_q + i) * H + h) * dr + er;
-      const float a = (float)__builtin_bit_cast(__bf16, src[0]), c = (float)__builtin_bit_cast(__bf16, src[1]);
-      const double ang = rope_angle(er >> 1, q_pos[3 * i], q_pos[3 * i + 1], q_pos[3 * i + 2], rope);
-      const float cs = (float)cos(ang), sn = (float)sin(ang);
-      x0 = fmaf(a, cs, -(c * sn));
-      x1 = fmaf(a, sn, c * cs);
+      const int er = (ch - NQ) * 8;
+      const uint4 raw = *reinterpret_cast<const uint4*>(q_r + tok * dr + er);
+      const uint32_t in[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bf16x2 two = __builtin_bit_cast(bf16x2, in[k]);
+        const float a = (float)two[0], c = (float)two[1];
+        const double ang = rope_angle((er >> 1) + k, q_pos[3 * i], q_pos[3 * i + 1], q_pos[3 * i + 2], rope);
+        const float cs = (float)cos(ang), sn = (float)sin(ang);
+        o[k] = bf16x2_bits(to_bf16x2(fmaf(a, cs, -(c * sn)), fmaf(a, sn, c * cs)));
+      }
+      val = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
-  *reinterpret_cast<uint32_t*>(qt + rowg * dqk + 2 * pr) = bf16x2_bits(to_bf16x2(x0, x1));
+  *reinterpret_cast<uint4*>(qt + ((int64_t)bh * rows_pad_h + i) * (nch * 8) + ch * 8) = val;
 }
 
 // Per-head keys and values from the latent cache (non-absorbed form):
 //   K[b, j, h, 0:dh]   = W_UK[h] c_j,   K[b, j, h, dh:dh+dr] = k_R,j
 //   V[b, j, h, :]      = W_UV[h] c_j
-// Workgroup (32 tokens, one head, K or V) with 4 wavefronts of 32 outputs:
-// C^T[o][token] = sum_k W[o][k] c[token][k] by bf16 MFMA 32x32x16, fp32
-// accumulation, one rounding to bf16.  The K workgroup also copies k_R.
+// Workgroup: 256 tokens (32 per wavefront) of one head, keys (blockIdx.z =
+// 0) or values (1).  The head's 128 x d_c weight block is staged once in LDS
+// (rows padded by 16 bytes so the 32 rows one b128 read touches spread over
+// the banks); each wavefront keeps its tokens' latent rows in registers as
+// the B operand and runs the four 32-output blocks through bf16 MFMA
+// 32x32x16 with fp32 accumulation and one rounding to bf16.  Key workgroups
+// also copy k_R into their tokens' K rows.  K and V hold exactly n_k keys
+// per sample.
 template <int DC>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(512)
 void mha_uplift_kernel(const u16* __restrict__ cache, int64_t cap, int n_k, int ntok, int H,
                        const u16* __restrict__ w_uk, const u16* __restrict__ w_uv,
                        u16* __restrict__ K, u16* __restrict__ V) {
-  constexpr int W = DC + 32, DH = 128, DQK = DH + 32;
+  constexpr int W = DC + 32, DH = 128, DQK = DH + 32, KS = DC / 16, WROW = DC * 2 + 16, CPR = DC / 8;
+  __shared__ __attribute__((aligned(16))) char wt[DH * WROW];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
-  const int tok0 = blockIdx.x * 32;
-  const int h = blockIdx.y >> 1;
-  const bool is_v = blockIdx.y & 1;
-  const int my_tok = min(tok0 + (lane & 31), ntok - 1);
+  const int h = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  const u16* wsrc = (is_v ? w_uv : w_uk) + (int64_t)h * DH * DC;
+  for (int idx = threadIdx.x; idx < DH * CPR; idx += 512) {
+    const int r = idx / CPR, ch = idx - r * CPR;
+    *reinterpret_cast<uint4*>(wt + r * WROW + ch * 16) = *reinterpret_cast<const uint4*>(wsrc + r * DC + ch * 8);
+  }
+  const int tok = blockIdx.x * 256 + wave * 32 + (lane & 31);
+  const int my_tok = min(tok, ntok - 1);
   const int b = my_tok / n_k, j = my_tok - b * n_k;
-  const u16* crow = cache + ((int64_t)b * cap + j) * W + half * 8;
-  const int o = wave * 32 + (lane & 31);
-  const u16* wrow = (is_v ? w_uv : w_uk) + ((int64_t)h * DH + o) * DC + half * 8;
-  f32x16 acc = {};
+  const u16* crow = cache + ((int64_t)b * cap + j) * W;
+  bf16x8 cf[KS];
 #pragma unroll
-  for (int k = 0; k < DC / 16; ++k)
-    acc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(wrow + k * 16), *reinterpret_cast<const bf16x8*>(crow + k * 16),
-                        acc);
-  // lane holds token (lane & 31), outputs wave*32 + 8g + 4*half + t
-  const int tok = tok0 + (lane & 31);
-  if (tok < ntok) {
-    const int tb = tok / n_k, tj = tok - tb * n_k;
-    const int64_t kv_row = ((int64_t)tb * n_k + tj) * H + h;   // K and V hold exactly n_k keys per sample
-    u16* dst = is_v ? V + kv_row * DH : K + kv_row * DQK;
+  for (int k = 0; k < KS; ++k) cf[k] = *reinterpret_cast<const bf16x8*>(crow + k * 16 + half * 8);
+  const int64_t kv_row = ((int64_t)b * n_k + j) * H + h;
+  u16* dst = is_v ? V + kv_row * DH : K + kv_row * DQK;
+  const bool live = tok < ntok;
+  __syncthreads();
+#pragma unroll 1
+  for (int ob = 0; ob < 4; ++ob) {
+    const char* a = wt + (ob * 32 + (lane & 31)) * WROW + half * 16;
+    f32x16 acc = {};
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int o0 = wave * 32 + gq * 8 + half * 4;
-      *reinterpret_cast<uint2*>(dst + o0) = make_uint2(bf16x2_bits(to_bf16x2(acc[4 * gq], acc[4 * gq + 1])),
-                                                       bf16x2_bits(to_bf16x2(acc[4 * gq + 2], acc[4 * gq + 3])));
+    for (int k = 0; k < KS; ++k) acc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(a + k * 32), cf[k], acc);
+    // lane holds its token's outputs 32*ob + 8g + 4*half + t, t = 0..3
+    if (live) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<uint2*>(dst + ob * 32 + g * 8 + half * 4) =
+            make_uint2(bf16x2_bits(to_bf16x2(acc[4 * g], acc[4 * g + 1])),
+                       bf16x2_bits(to_bf16x2(acc[4 * g + 2], acc[4 * g + 3])));
     }
-    if (!is_v && wave == 0) {   // the positional key, shared by every head
-      const u16* kr = cache + ((int64_t)tb * cap + tj) * W + DC + half * 16;
-      *reinterpret_cast<uint4*>(dst + DH + half * 16) = *reinterpret_cast<const uint4*>(kr);
-      *reinterpret_cast<uint4*>(dst + DH + half * 16 + 8) = *reinterpret_cast<const uint4*>(kr + 8);
-    }
+  }
+  if (!is_v && live) {   // the positional key, shared by every head
+    const uint4* kr = reinterpret_cast<const uint4*>(crow + DC + half * 16);
+    uint4* kd = reinterpret_cast<uint4*>(dst + DH + half * 16);
+    kd[0] = kr[0];
+    kd[1] = kr[1];
   }
 }
 
@@ -513,24 +529,28 @@ MhaPlan make_mha_plan(int B, int H, int n_q, int n_k, int dqk, bool expanded) {
 }
 
 hipError_t launch_mha_prep_q(const MhaPlan& p, const MhaQueryArgs& a, hipStream_t s) {
-  const int64_t work = (int64_t)p.B * p.H * p.rows_pad_h * (p.dqk / 2);
-  mha::mha_prep_q_kernel<<<dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s>>>(
-      (const u16*)a.q, (const u16*)a.q_r, a.q_pos, p.B, p.H, p.n_q, 128, p.dqk - 128, p.rows_pad_h, a.rope,
-      (u16*)((char*)a.workspace + p.off_qt));
+  const int nch = p.dqk / 8;
+  const dim3 grid((unsigned)((p.rows_pad_h * nch + 255) / 256), (unsigned)(p.B * p.H));
+  mha::mha_prep_q_kernel<<<grid, dim3(256), 0, s>>>((const u16*)a.q, (const u16*)a.q_r, a.q_pos, p.H, p.n_q,
+                                                    p.dqk - 128, p.rows_pad_h, a.rope,
+                                                    (u16*)((char*)a.workspace + p.off_qt));
   return hipGetLastError();
 }
 
 hipError_t launch_mha_uplift(const MhaPlan& p, const MhaUpliftArgs& a, hipStream_t s) {
   char* ws = (char*)a.workspace;
   const int ntok = p.B * p.n_k;
-  const dim3 grid((ntok + 31) / 32, 2 * p.H), block(256);
+  const dim3 grid((ntok + 255) / 256, p.H, 2), block(512);
   u16* K = (u16*)(ws + p.off_k);
   u16* V = (u16*)(ws + p.off_v);
+  const u16* c = (const u16*)a.cache;
+  const u16* wk = (const u16*)a.w_uk;
+  const u16* wv = (const u16*)a.w_uv;
   switch (a.d_c) {
-    case 64: mha::mha_uplift_kernel<64><<<grid, block, 0, s>>>((const u16*)a.cache, a.cap, p.n_k, ntok, p.H, (const u16*)a.w_uk, (const u16*)a.w_uv, K, V); break;
-    case 128: mha::mha_uplift_kernel<128><<<grid, block, 0, s>>>((const u16*)a.cache, a.cap, p.n_k, ntok, p.H, (const u16*)a.w_uk, (const u16*)a.w_uv, K, V); break;
-    case 192: mha::mha_uplift_kernel<192><<<grid, block, 0, s>>>((const u16*)a.cache, a.cap, p.n_k, ntok, p.H, (const u16*)a.w_uk, (const u16*)a.w_uv, K, V); break;
-    case 256: mha::mha_uplift_kernel<256><<<grid, block, 0, s>>>((const u16*)a.cache, a.cap, p.n_k, ntok, p.H, (const u16*)a.w_uk, (const u16*)a.w_uv, K, V); break;
+    case 64: mha::mha_uplift_kernel<64><<<grid, block, 0, s>>>(c, a.cap, p.n_k, ntok, p.H, wk, wv, K, V); break;
+    case 128: mha::mha_uplift_kernel<128><<<grid, block, 0, s>>>(c, a.cap, p.n_k, ntok, p.H, wk, wv, K, V); break;
+    case 192: mha::mha_uplift_kernel<192><<<grid, block, 0, s>>>(c, a.cap, p.n_k, ntok, p.H, wk, wv, K, V); break;
+    case 256: mha::mha_uplift_kernel<256><<<grid, block, 0, s>>>(c, a.cap, p.n_k, ntok, p.H, wk, wv, K, V); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
