@@ -9,14 +9,16 @@
 //    and V_h = C W_UV[h]^T are materialised from the latent cache once per
 //    call, then the same attention runs with d_qk = d_h + d_r.
 //
-// The attention kernel has the wavefront roles of attend.hip (see there):
-// a workgroup owns 256 rows of one (batch, head), in four groups of 64 with
-// a score wavefront (q in registers, S^T = K q^T by bf16 32x32x16 MFMA,
-// p = 2^(s - m), P to LDS) and a value wavefront (O^T += V^T P^T, V^T read
-// transposed from LDS) on each SIMD.  Per-head rows [k || v] are staged by
-// direct-to-LDS loads in 32-key tiles (three buffers: scored, multiplied,
-// loading); a key row is d_qk + d_v values, so 64-key tiles would not fit
-// the LDS three times over.  Partial softmax states per (workgroup, row
+// The attention kernel has the wavefront roles of attend.hip: a workgroup
+// owns 256 rows of one (batch, head), in four groups of 64 with a score
+// wavefront (q in registers, S^T = K q^T by bf16 32x32x16 MFMA,
+// p = 2^(qscale*s - m), P to LDS) and a value wavefront (O^T += V^T P^T, V^T
+// read transposed from LDS) on each SIMD.  Keys and values are staged by
+// direct-to-LDS loads in 64-key tiles, in separate double buffers: in step
+// k the score side reads K of tile k while K of tile k+1 arrives, and the
+// value side reads V of tile k-1 while V of tile k arrives, so two buffers
+// of each serve where a combined [k || v] row would need three (which would
+// not fit the LDS at 64 keys).  Partial softmax states per (workgroup, row
 // block) are merged by mha_merge_kernel.
 #include "mla_common.h"
 #include "mla_kernels.h"
@@ -33,56 +35,84 @@ __device__ inline void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  //
 constexpr int kWaves = 8;          // wavefronts per workgroup
 constexpr int kGroups = 4;         // row groups (score + value wavefront each)
 constexpr int kGroupRows = 64;     // rows per group: two 32-row MFMA blocks
-constexpr int kBN = 32;            // keys per tile
+constexpr int kBN = 64;            // keys per tile: two 32-key MFMA blocks
 constexpr int kDV = 128;           // value width (head_dim)
+
+// LDS staging of one tensor's rows of a 64-key tile: rows padded by one
+// 16-byte slot (odd stride in 16-byte units); one 64-lane direct-to-LDS
+// load copies ROWS whole rows, the pad lane re-reading the row's last chunk.
+template <int D>
+struct Rows {
+  static constexpr int NCH = D / 8;                 // 16-byte chunks of a row
+  static constexpr int NSLOT = NCH + 1;
+  static constexpr int ROWB = NSLOT * 16;           // LDS bytes per key
+  static constexpr int BUF = kBN * ROWB;            // LDS bytes per tile
+  static constexpr int ROWS = 64 / NSLOT;           // rows per load
+  static constexpr int NLOAD = (kBN + ROWS - 1) / ROWS;
+  static constexpr int PER_WAVE = (NLOAD + kWaves - 1) / kWaves;
+  static_assert(ROWS >= 1 && (NSLOT & 1), "a row fits one load, odd slot stride");
+};
 
 template <int DQK>
 struct Tile {
-  static constexpr int NK = DQK / 8;          // 16-byte chunks of a key row
-  static constexpr int NV = kDV / 8;          // 16-byte chunks of a value row
-  static constexpr int NCH = NK + NV;         // chunks of the staged [k || v] row
-  static constexpr int NSLOT = NCH + 1;       // plus one pad slot (odd stride in 16-byte units)
-  static constexpr int ROWB = NSLOT * 16;     // LDS bytes per key
-  static constexpr int TILEB = kBN * ROWB;    // LDS bytes per tile buffer
-  static constexpr int LPW = kBN / kWaves;    // one row per 64-lane load; loads per wavefront per tile
+  using K = Rows<DQK>;
+  using V = Rows<kDV>;
   static constexpr int KS = DQK / 16;         // score k-steps
   static constexpr int CB = kDV / 32;         // 32-column blocks of O^T
-  static constexpr int PBUF = kGroups * 2 * 2 * 64 * 16;   // P bytes of one tile
-  static_assert(NSLOT <= 64 && (NSLOT & 1), "a staged row fits one load, odd slot stride");
-  static_assert(3 * TILEB + 2 * PBUF <= 160 * 1024, "buffers exceed LDS");
+  static constexpr int PBUF = kGroups * 2 * 2 * 2 * 64 * 16;   // P bytes of one tile (group, kb, qb, part, lane)
+  static_assert(2 * K::BUF + 2 * V::BUF + 2 * PBUF <= 160 * 1024, "buffers exceed LDS");
 };
 
+// Per-lane slot of the direct-to-LDS copies of one tensor.
+struct LaneCopy {
+  uint32_t chunk;   // byte offset of the lane's chunk inside its row
+  int row;          // row of the load the lane copies (>= ROWS: idle)
+};
+
+template <int D>
+__device__ inline LaneCopy lane_copy(int lane) {
+  using R = Rows<D>;
+  LaneCopy lc;
+  lc.row = lane / R::NSLOT;
+  lc.chunk = (uint32_t)min(lane - lc.row * R::NSLOT, R::NCH - 1) * 16;
+  return lc;
+}
+
 struct Ctx {
-  const char* src;       // key 0 of this (batch, head) in K or V, per lane
-  uint32_t row_bytes;    // bytes between consecutive keys of the lane's tensor
-  uint32_t lane_src;     // byte offset of the lane's chunk inside its k or v row
-  bool lane_v, lane_on;  // chunk comes from V; lane copies a chunk at all
+  const char* kbase;     // key 0 of this (batch, head) in K
+  const char* vbase;     // key 0 of this (batch, head) in V
+  uint32_t krow, vrow;   // bytes between consecutive keys in K and V
+  LaneCopy kc, vc;
   int n_k;
   int wave, lane, half, group;
   int s_off, v_off;      // LDS operand offsets inside a tile
 };
 
-// Enqueue this wavefront's direct-to-LDS loads of tile t: load i copies key
-// row (wave + kWaves * i); lane l writes slot l of that staged row (the pad
-// slot re-reads the last value chunk).  Keys past n_k re-read key n_k - 1.
-// Offsets are 32-bit: one (batch, head)'s keys span less than 4 GiB.
-template <int DQK>
-__device__ inline void issue_tile(const Ctx& c, int t, char* tile) {
-  using L = Tile<DQK>;
+// Enqueue this wavefront's share of the direct-to-LDS loads of tile t of one
+// tensor: load ld copies rows [ld*ROWS, ld*ROWS + ROWS).  Keys past n_k
+// re-read key n_k - 1 (their scores are masked).  Offsets are 32-bit: one
+// (batch, head)'s keys span less than 4 GiB.
+template <int D>
+__device__ inline void issue_rows(const Ctx& c, const char* base, uint32_t row_bytes, const LaneCopy& lc, int t,
+                                  char* buf) {
+  using R = Rows<D>;
 #pragma unroll
-  for (int i = 0; i < L::LPW; ++i) {
-    const int row = c.wave + kWaves * i;
-    const uint32_t key = (uint32_t)min(t * kBN + row, c.n_k - 1);
-    if (c.lane_on)
-      __builtin_amdgcn_global_load_lds(c.src + (key * c.row_bytes + c.lane_src), (lds_void*)(tile + row * L::ROWB),
-                                       16, 0, 0);
+  for (int i = 0; i < R::PER_WAVE; ++i) {
+    const int ld = c.wave + kWaves * i;
+    if (ld < R::NLOAD) {
+      const int row0 = ld * R::ROWS;
+      const uint32_t key = (uint32_t)min(t * kBN + row0 + lc.row, c.n_k - 1);
+      if (lc.row < R::ROWS && row0 + lc.row < kBN)
+        __builtin_amdgcn_global_load_lds(base + (key * row_bytes + lc.chunk), (lds_void*)(buf + row0 * R::ROWB), 16,
+                                         0, 0);
+    }
   }
 }
 
 enum class Pass { kSingle, kMax, kAccum };
 
-__device__ __forceinline__ int p_slot(int g, int qb, int part, int lane) {
-  return (((g * 2 + qb) * 2 + part) * 64 + lane) * 16;
+__device__ __forceinline__ int p_slot(int g, int kb, int qb, int part, int lane) {
+  return ((((g * 2 + kb) * 2 + qb) * 2 + part) * 64 + lane) * 16;
 }
 
 __device__ __forceinline__ void mask_block(f32x16& s, int n_valid, int half) {
@@ -109,53 +139,55 @@ struct ScoreState {
   float l_run[2];
 };
 
+// Scores of tile t: S^T = K q^T for the two 32-key blocks and two 32-row
+// blocks of the group, then p = 2^(qscale*s - m) to the P buffer as the
+// B operand of the value product.
 template <int DQK, Pass P>
-__device__ __forceinline__ void score_tile(ScoreState<DQK>& st, const char* tile, char* pbuf, int t, bool first,
+__device__ __forceinline__ void score_tile(ScoreState<DQK>& st, const char* kbuf, char* pbuf, int t, bool first,
                                            const Ctx& c) {
   using L = Tile<DQK>;
-  constexpr int KS = L::KS, PF = 4;
-  const char* kbase = tile + c.s_off;
-  f32x16 s[2] = {f32x16{}, f32x16{}};
-  bf16x8 a[PF];
+  constexpr int KS = L::KS;
 #pragma unroll
-  for (int i = 0; i < PF; ++i) a[i] = *reinterpret_cast<const bf16x8*>(kbase + i * 32);
+  for (int kb = 0; kb < 2; ++kb) {
+    const char* kbase = kbuf + kb * 32 * L::K::ROWB + c.s_off;
+    f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const bf16x8 cur = a[ks % PF];
-    if (ks + PF < KS) a[ks % PF] = *reinterpret_cast<const bf16x8*>(kbase + (ks + PF) * 32);
-    s[0] = mfma_32x32x16(cur, st.qf[0][ks], s[0]);
-    s[1] = mfma_32x32x16(cur, st.qf[1][ks], s[1]);
-  }
-  const int left = c.n_k - t * kBN;
-  if (left < 32) {
-    mask_block(s[0], left, c.half);
-    mask_block(s[1], left, c.half);
-  }
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    if (P == Pass::kMax) {
-      st.m_ref[qb] = fmaxf(st.m_ref[qb], block_max(s[qb]) * st.qscale);
-      continue;
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbase + ks * 32);
+      s[0] = mfma_32x32x16(a, st.qf[0][ks], s[0]);
+      s[1] = mfma_32x32x16(a, st.qf[1][ks], s[1]);
     }
-    if (P == Pass::kSingle && first) st.m_ref[qb] = block_max(s[qb]) * st.qscale;
-    const float m = st.m_ref[qb];
-    float p[16];
+    const int left = c.n_k - t * kBN - kb * 32;
+    if (left < 32) {
+      mask_block(s[0], left, c.half);
+      mask_block(s[1], left, c.half);
+    }
 #pragma unroll
-    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(s[qb][v], st.qscale, -m));
-    float q[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) q[v] = p[2 * v] + p[2 * v + 1];
-    st.l_run[qb] += ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
-#pragma unroll
-    for (int part = 0; part < 2; ++part) {
-      bf16x8 pv;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2 two = to_bf16x2(p[part * 8 + e], p[part * 8 + e + 1]);
-        pv[e] = two[0];
-        pv[e + 1] = two[1];
+    for (int qb = 0; qb < 2; ++qb) {
+      if (P == Pass::kMax) {
+        st.m_ref[qb] = fmaxf(st.m_ref[qb], block_max(s[qb]) * st.qscale);
+        continue;
       }
-      *reinterpret_cast<bf16x8*>(pbuf + p_slot(c.group, qb, part, c.lane)) = pv;
+      if (P == Pass::kSingle && first && kb == 0) st.m_ref[qb] = block_max(s[qb]) * st.qscale;
+      const float m = st.m_ref[qb];
+      float p[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(s[qb][v], st.qscale, -m));
+      float q[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) q[v] = p[2 * v] + p[2 * v + 1];
+      st.l_run[qb] += ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        bf16x8 pv;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 two = to_bf16x2(p[part * 8 + e], p[part * 8 + e + 1]);
+          pv[e] = two[0];
+          pv[e + 1] = two[1];
+        }
+        *reinterpret_cast<bf16x8*>(pbuf + p_slot(c.group, kb, qb, part, c.lane)) = pv;
+      }
     }
   }
 }
@@ -164,37 +196,44 @@ struct ValueState {
   f32x16 oacc[2][kDV / 32];
 };
 
+// O^T += V^T P^T for the tile's two 32-key blocks; V^T is read transposed
+// from LDS (ds_read_tr16_b64), the key order inside each 16-key step
+// matching the order in which the score wavefront stored P.
 template <int DQK>
-__device__ __forceinline__ void value_tile(ValueState& st, const char* tile, const char* pbuf, const Ctx& c) {
+__device__ __forceinline__ void value_tile(ValueState& st, const char* vbuf, const char* pbuf, const Ctx& c) {
   using L = Tile<DQK>;
-  const char* blk = tile + c.v_off;
+  constexpr int VR = L::V::ROWB;
 #pragma unroll
-  for (int part = 0; part < 2; ++part) {
-    const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(pbuf + p_slot(c.group, 0, part, c.lane));
-    const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(pbuf + p_slot(c.group, 1, part, c.lane));
-    const char* vbase = blk + part * 16 * L::ROWB;
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int cb = 0; cb < L::CB; ++cb) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + cb * 64));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + 8 * L::ROWB + cb * 64));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      st.oacc[0][cb] = mfma_32x32x16(a, p0, st.oacc[0][cb]);
-      st.oacc[1][cb] = mfma_32x32x16(a, p1, st.oacc[1][cb]);
+    for (int part = 0; part < 2; ++part) {
+      const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(pbuf + p_slot(c.group, kb, 0, part, c.lane));
+      const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(pbuf + p_slot(c.group, kb, 1, part, c.lane));
+      const char* vb = vbuf + (kb * 32 + part * 16) * VR + c.v_off;
+#pragma unroll
+      for (int cb = 0; cb < L::CB; ++cb) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + cb * 64));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * VR + cb * 64));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        st.oacc[0][cb] = mfma_32x32x16(a, p0, st.oacc[0][cb]);
+        st.oacc[1][cb] = mfma_32x32x16(a, p1, st.oacc[1][cb]);
+      }
     }
-  }
 }
 
-// One step: start tile k+1 into `nxt`; score tile k (`cur`, P to P[k % 2])
-// or multiply tile k-1 (`prv`, P from P[(k-1) % 2]); wait; barrier.  Steps
-// k = 0 .. n; returns true after step n.
+// Step k of a sweep over tiles t0 .. t0+n-1: start K of tile k+1 and V of
+// tile k; the score wavefront scores tile k (K buffer k % 2, P buffer k % 2),
+// the value wavefront multiplies tile k-1 (V buffer (k-1) % 2, P buffer
+// (k-1) % 2); wait; barrier.  Steps k = 0 .. n; true after step n.
 template <int DQK, Pass P, bool SCORE, class State>
-__device__ __forceinline__ bool sweep_step(State& st, int k, int n, int t0, char* cur, char* nxt, char* prv,
-                                           char* pb0, char* pb1, const Ctx& c) {
-  if (k + 1 < n) issue_tile<DQK>(c, t0 + k + 1, nxt);
+__device__ __forceinline__ bool sweep_step(State& st, int k, int n, int t0, char* kcur, char* knxt, char* vload,
+                                           char* vprev, char* pcur, char* pprev, const Ctx& c) {
+  if (k + 1 < n) issue_rows<DQK>(c, c.kbase, c.krow, c.kc, t0 + k + 1, knxt);
+  if (P != Pass::kMax && k < n) issue_rows<kDV>(c, c.vbase, c.vrow, c.vc, t0 + k, vload);
   if constexpr (SCORE) {
-    if (k < n) score_tile<DQK, P>(st, cur, (k & 1) ? pb1 : pb0, t0 + k, k == 0, c);
+    if (k < n) score_tile<DQK, P>(st, kcur, pcur, t0 + k, k == 0, c);
   } else {
-    if (P != Pass::kMax && k >= 1) value_tile<DQK>(st, prv, (k & 1) ? pb0 : pb1, c);
+    if (P != Pass::kMax && k >= 1) value_tile<DQK>(st, vprev, pprev, c);
   }
   wait_vmcnt0();
   __syncthreads();
@@ -202,22 +241,21 @@ __device__ __forceinline__ bool sweep_step(State& st, int k, int n, int t0, char
 }
 
 template <int DQK, Pass P, bool SCORE, class State>
-__device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* k2, char* pb0, char* pb1, int t0, int t1,
-                                      const Ctx& c) {
+__device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* v0, char* v1, char* pb0, char* pb1,
+                                      int t0, int t1, const Ctx& c) {
   const int n = t1 - t0;
-  issue_tile<DQK>(c, t0, k0);
+  issue_rows<DQK>(c, c.kbase, c.krow, c.kc, t0, k0);
   wait_vmcnt0();
   __syncthreads();
 #pragma unroll 1
-  for (int k = 0;; k += 3) {
-    if (sweep_step<DQK, P, SCORE>(st, k, n, t0, k0, k1, k2, pb0, pb1, c)) break;
-    if (sweep_step<DQK, P, SCORE>(st, k + 1, n, t0, k1, k2, k0, pb0, pb1, c)) break;
-    if (sweep_step<DQK, P, SCORE>(st, k + 2, n, t0, k2, k0, k1, pb0, pb1, c)) break;
+  for (int k = 0;; k += 2) {
+    if (sweep_step<DQK, P, SCORE>(st, k, n, t0, k0, k1, v0, v1, pb0, pb1, c)) break;
+    if (sweep_step<DQK, P, SCORE>(st, k + 1, n, t0, k1, k0, v1, v0, pb1, pb0, c)) break;
   }
 }
 
 struct Problem {
-  const u16* q;          // absorbed/scaled queries [B*H][rows_pad_h][DQK]
+  const u16* q;          // queries [B*H][rows_pad_h][DQK], bf16, unscaled
   const u16* k;          // [B, cap, H, DQK]
   const u16* v;          // [B, cap, H, kDV]
   int64_t cap;
@@ -230,19 +268,19 @@ struct Problem {
   float* part_ml;        // [slots][256][2]
 };
 
-// Row block rb = (b*H + h) * rb_per_bh + rbl; units rb*T .. rb*T + T - 1.
+// Row block rb = (b*H + h) * rb_per_bh + rbl; its units are rb*T .. rb*T + T - 1.
 template <int DQK>
 __device__ __forceinline__ void begin_segment(Ctx& c, const Problem& pr, int64_t rb) {
   const int64_t bh = rb / pr.rb_per_bh;
   const int b = (int)(bh / pr.H), h = (int)(bh - (int64_t)b * pr.H);
   const int64_t tok0 = (int64_t)b * pr.cap * pr.H + h;
-  c.src = c.lane_v ? reinterpret_cast<const char*>(pr.v + tok0 * kDV)
-                   : reinterpret_cast<const char*>(pr.k + tok0 * DQK);
+  c.kbase = reinterpret_cast<const char*>(pr.k + tok0 * DQK);
+  c.vbase = reinterpret_cast<const char*>(pr.v + tok0 * kDV);
 }
 
 template <int DQK, bool SCORE>
-__device__ __forceinline__ void role(Ctx& c, const Problem& pr, int64_t w, char* k0, char* k1, char* k2, char* pb0,
-                                     char* pb1) {
+__device__ __forceinline__ void role(Ctx& c, const Problem& pr, int64_t w, char* k0, char* k1, char* v0, char* v1,
+                                     char* pb0, char* pb1) {
   using L = Tile<DQK>;
   int64_t u = unit_begin(w, pr.U, pr.G);
   const int64_t u_end = unit_begin(w + 1, pr.U, pr.G);
@@ -267,7 +305,7 @@ __device__ __forceinline__ void role(Ctx& c, const Problem& pr, int64_t w, char*
         ss.m_ref[qb] = -INFINITY;
       }
       ss.qscale = pr.qscale;
-      sweep<DQK, Pass::kSingle, true>(ss, k0, k1, k2, pb0, pb1, t0, t1, c);
+      sweep<DQK, Pass::kSingle, true>(ss, k0, k1, v0, v1, pb0, pb1, t0, t1, c);
       const float lim = __builtin_amdgcn_exp2f(pr.headroom);
       bad = !(ss.l_run[0] <= lim) || !(ss.l_run[1] <= lim);
     } else {
@@ -275,7 +313,7 @@ __device__ __forceinline__ void role(Ctx& c, const Problem& pr, int64_t w, char*
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int cb = 0; cb < L::CB; ++cb) vs.oacc[qb][cb] = f32x16{};
-      sweep<DQK, Pass::kSingle, false>(vs, k0, k1, k2, pb0, pb1, t0, t1, c);
+      sweep<DQK, Pass::kSingle, false>(vs, k0, k1, v0, v1, pb0, pb1, t0, t1, c);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -287,16 +325,16 @@ __device__ __forceinline__ void role(Ctx& c, const Problem& pr, int64_t w, char*
       // exact two-pass evaluation of this segment: the true max, then accumulation
       if constexpr (SCORE) {
         ss.m_ref[0] = ss.m_ref[1] = -INFINITY;
-        sweep<DQK, Pass::kMax, true>(ss, k0, k1, k2, pb0, pb1, t0, t1, c);
+        sweep<DQK, Pass::kMax, true>(ss, k0, k1, v0, v1, pb0, pb1, t0, t1, c);
         ss.l_run[0] = ss.l_run[1] = 0.f;
-        sweep<DQK, Pass::kAccum, true>(ss, k0, k1, k2, pb0, pb1, t0, t1, c);
+        sweep<DQK, Pass::kAccum, true>(ss, k0, k1, v0, v1, pb0, pb1, t0, t1, c);
       } else {
-        sweep<DQK, Pass::kMax, false>(vs, k0, k1, k2, pb0, pb1, t0, t1, c);
+        sweep<DQK, Pass::kMax, false>(vs, k0, k1, v0, v1, pb0, pb1, t0, t1, c);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
           for (int cb = 0; cb < L::CB; ++cb) vs.oacc[qb][cb] = f32x16{};
-        sweep<DQK, Pass::kAccum, false>(vs, k0, k1, k2, pb0, pb1, t0, t1, c);
+        sweep<DQK, Pass::kAccum, false>(vs, k0, k1, v0, v1, pb0, pb1, t0, t1, c);
       }
     }
     const int64_t slot = seg_slot(w, rb);
@@ -329,29 +367,29 @@ template <int DQK>
 __global__ __launch_bounds__(kWaves * 64, 1)
 void mha_attend_kernel(Problem pr) {
   using L = Tile<DQK>;
-  __shared__ __attribute__((aligned(1024))) char kbuf0[L::TILEB];
-  __shared__ __attribute__((aligned(1024))) char kbuf1[L::TILEB];
-  __shared__ __attribute__((aligned(1024))) char kbuf2[L::TILEB];
+  __shared__ __attribute__((aligned(1024))) char kbuf0[L::K::BUF];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[L::K::BUF];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[L::V::BUF];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[L::V::BUF];
   __shared__ __attribute__((aligned(1024))) char pbuf0[L::PBUF];
   __shared__ __attribute__((aligned(1024))) char pbuf1[L::PBUF];
   Ctx c;
   c.n_k = pr.n_k;
+  c.krow = (uint32_t)pr.H * DQK * 2;
+  c.vrow = (uint32_t)pr.H * kDV * 2;
   c.lane = threadIdx.x & 63;
   c.half = c.lane >> 5;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool scorer = c.wave < kGroups;   // wavefronts w and w + 4 share a SIMD
   c.group = c.wave & (kGroups - 1);
-  const int ch = min(c.lane, L::NCH - 1);  // the pad lane re-copies the last chunk
-  c.lane_on = c.lane < L::NSLOT;
-  c.lane_v = ch >= L::NK;
-  c.lane_src = (uint32_t)((c.lane_v ? ch - L::NK : ch) * 16);
-  c.row_bytes = (uint32_t)pr.H * (c.lane_v ? kDV : DQK) * 2;
-  c.s_off = (c.lane & 31) * L::ROWB + c.half * 16;
+  c.kc = lane_copy<DQK>(c.lane);
+  c.vc = lane_copy<kDV>(c.lane);
+  c.s_off = (c.lane & 31) * L::K::ROWB + c.half * 16;
   const int g = c.lane >> 4, j = c.lane & 15;
-  c.v_off = ((g >> 1) * 4 + (j >> 2)) * L::ROWB + (16 * (g & 1) + 4 * (j & 3)) * 2 + DQK * 2;
+  c.v_off = ((g >> 1) * 4 + (j >> 2)) * L::V::ROWB + (16 * (g & 1) + 4 * (j & 3)) * 2;
   const int64_t w = (int64_t)pr.G - 1 - blockIdx.x;
-  if (scorer) role<DQK, true>(c, pr, w, kbuf0, kbuf1, kbuf2, pbuf0, pbuf1);
-  else role<DQK, false>(c, pr, w, kbuf0, kbuf1, kbuf2, pbuf0, pbuf1);
+  if (scorer) role<DQK, true>(c, pr, w, kbuf0, kbuf1, vbuf0, vbuf1, pbuf0, pbuf1);
+  else role<DQK, false>(c, pr, w, kbuf0, kbuf1, vbuf0, vbuf1, pbuf0, pbuf1);
 }
 
 // out[b, i, h, :] = sum_s 2^(m_s - M) L_s / sum_s 2^(m_s - M) l_s over the
