@@ -206,7 +206,7 @@ int32_t chunk_attend_impl(const mla_dims* dims, int32_t in_dtype, int32_t out_dt
 int32_t check_mha_sizes(int32_t batch, int32_t n_heads, int32_t n_q, int32_t n_k, int32_t dqk) {
   if (batch < 1 || n_heads < 1) return fail(MLA_ERR_INVALID_ARG, "batch and n_heads must be >= 1");
   if (n_heads > 4096) return fail(MLA_ERR_UNSUPPORTED, "n_heads must be <= 4096 (got %d)", n_heads);
-  if ((int64_t)batch * n_heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch * n_heads must be <= 65535");
+  if (batch > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch must be <= 65535");
   if (n_q < 1) return fail(MLA_ERR_INVALID_ARG, "n_q must be >= 1 (got %d)", n_q);
   if (n_k < n_q) return fail(MLA_ERR_INVALID_ARG, "n_k (%d) must be >= n_q (%d): the current chunk is part of the keys", n_k, n_q);
   if ((int64_t)batch * n_heads * ((int64_t)n_q + 255) > (int64_t)1 << 30)

@@ -440,8 +440,9 @@ void mha_merge_kernel(const float* __restrict__ part_L, const float* __restrict_
 // bf16(qfull[b, i, h, e]) with qfull = q (dense: an exact copy) or
 // [q_h || RoPE3D(p_i) q_r,h] (non-absorbed latent); rows past n_q are zero.
 // The softmax scale is applied to the fp32 scores, so no query is rounded
-// after scaling.  Thread = 8 consecutive elements (16 bytes) of one row;
-// grid.y = b*H + h.
+// after scaling.  Thread = 8 consecutive elements (16 bytes) of row i of
+// sample blockIdx.y, for heads 4*blockIdx.z .. 4*blockIdx.z + 3 in turn (a
+// rotated chunk's angles are evaluated once, in fp64, for those heads).
 __global__ __launch_bounds__(256)
 void mha_prep_q_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r, const int* __restrict__ q_pos,
                        int H, int n_q, int dr, int rows_pad_h, RopeSpec rope, u16* __restrict__ qt) {
@@ -450,30 +451,40 @@ void mha_prep_q_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r, c
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= rows_pad_h * nch) return;
   const int i = idx / nch, ch = idx - i * nch;
-  const int bh = blockIdx.y;
-  const int b = bh / H, h = bh - b * H;
-  uint4 val = make_uint4(0, 0, 0, 0);
-  if (i < n_q) {
-    const int64_t tok = ((int64_t)b * n_q + i) * H + h;
-    if (ch < NQ) {
-      val = *reinterpret_cast<const uint4*>(q + tok * DH + ch * 8);
-    } else {
-      const int er = (ch - NQ) * 8;
-      const uint4 raw = *reinterpret_cast<const uint4*>(q_r + tok * dr + er);
-      const uint32_t in[4] = {raw.x, raw.y, raw.z, raw.w};
-      uint32_t o[4];
+  const int b = blockIdx.y;
+  const bool live = i < n_q, rot = ch >= NQ;
+  const int er = (ch - NQ) * 8;
+  float cs[4], sn[4];
+  if (live && rot) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const bf16x2 two = __builtin_bit_cast(bf16x2, in[k]);
-        const float a = (float)two[0], c = (float)two[1];
-        const double ang = rope_angle((er >> 1) + k, q_pos[3 * i], q_pos[3 * i + 1], q_pos[3 * i + 2], rope);
-        const float cs = (float)cos(ang), sn = (float)sin(ang);
-        o[k] = bf16x2_bits(to_bf16x2(fmaf(a, cs, -(c * sn)), fmaf(a, sn, c * cs)));
-      }
-      val = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int k = 0; k < 4; ++k) {
+      const double ang = rope_angle((er >> 1) + k, q_pos[3 * i], q_pos[3 * i + 1], q_pos[3 * i + 2], rope);
+      cs[k] = (float)cos(ang);
+      sn[k] = (float)sin(ang);
     }
   }
-  *reinterpret_cast<uint4*>(qt + ((int64_t)bh * rows_pad_h + i) * (nch * 8) + ch * 8) = val;
+  for (int h = blockIdx.z * 4; h < min(H, blockIdx.z * 4 + 4); ++h) {
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (live) {
+      const int64_t tok = ((int64_t)b * n_q + i) * H + h;
+      if (!rot) {
+        val = *reinterpret_cast<const uint4*>(q + tok * DH + ch * 8);
+      } else {
+        const uint4 raw = *reinterpret_cast<const uint4*>(q_r + tok * dr + er);
+        const uint32_t in[4] = {raw.x, raw.y, raw.z, raw.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const bf16x2 two = __builtin_bit_cast(bf16x2, in[k]);
+          const float a = (float)two[0], c = (float)two[1];
+          o[k] = bf16x2_bits(to_bf16x2(fmaf(a, cs[k], -(c * sn[k])), fmaf(a, sn[k], c * cs[k])));
+        }
+        val = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+    const int64_t bh = (int64_t)b * H + h;
+    *reinterpret_cast<uint4*>(qt + (bh * rows_pad_h + i) * (nch * 8) + ch * 8) = val;
+  }
 }
 
 // Per-head keys and values from the latent cache (non-absorbed form):
@@ -568,7 +579,7 @@ MhaPlan make_mha_plan(int B, int H, int n_q, int n_k, int dqk, bool expanded) {
 
 hipError_t launch_mha_prep_q(const MhaPlan& p, const MhaQueryArgs& a, hipStream_t s) {
   const int nch = p.dqk / 8;
-  const dim3 grid((unsigned)((p.rows_pad_h * nch + 255) / 256), (unsigned)(p.B * p.H));
+  const dim3 grid((unsigned)((p.rows_pad_h * nch + 255) / 256), (unsigned)p.B, (unsigned)((p.H + 3) / 4));
   mha::mha_prep_q_kernel<<<grid, dim3(256), 0, s>>>((const u16*)a.q, (const u16*)a.q_r, a.q_pos, p.H, p.n_q,
                                                     p.dqk - 128, p.rows_pad_h, a.rope,
                                                     (u16*)((char*)a.workspace + p.off_qt));

@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def short_name(name: str) -> str:
-    m = re.search(r"mla::(\w+<[^>]*>)", name)
+    m = re.search(r"mla::(?:\w+::)*(\w+(?:<[^>]*>)?)\(", name)
     if m:
         return m.group(1)
     return name.split("(")[0][-80:]
