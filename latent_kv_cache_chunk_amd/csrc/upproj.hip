@@ -46,28 +46,43 @@ void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restric
   }
   const float inv_l = 1.f / lsum;
 
+  // L of this lane's row and columns {ks*16 + half*8 + e}: one pass over the
+  // segments, each segment's weight computed once and all of its columns
+  // loaded together (rows of short chunks can have over a hundred segments).
+  float lc[KSTEPS][8];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lc[ks][e] = 0.f;
+#pragma unroll 2
+  for (int64_t w = wa; w <= wb; ++w) {
+    const int64_t sl = seg_slot(w, rb);
+    const float wgt = exp2f(part_ml[(sl * kRowsPerBlock + rl) * 2] - M) * inv_l;
+    const float* src = part_L + (sl * kRowsPerBlock + rl) * DC + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + ks * 16);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + ks * 16 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lc[ks][e] = fmaf(wgt, x0[e], lc[ks][e]);
+        lc[ks][4 + e] = fmaf(wgt, x1[e], lc[ks][4 + e]);
+      }
+    }
+  }
+
   f32x16 acc[DH / 32];
 #pragma unroll
   for (int db = 0; db < DH / 32; ++db) acc[db] = f32x16{};
   const u16* wv = w_uv + (int64_t)h * DH * DC;
-
-#pragma unroll 2
+#pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
     const int c0 = ks * 16 + half * 8;
-    float lc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int64_t w = wa; w <= wb; ++w) {
-      const int64_t sl = seg_slot(w, rb);
-      const float wgt = exp2f(part_ml[(sl * kRowsPerBlock + rl) * 2] - M) * inv_l;
-      const f32x4* src = reinterpret_cast<const f32x4*>(part_L + (sl * kRowsPerBlock + rl) * DC + c0);
-      const f32x4 x0 = src[0], x1 = src[1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { lc[e] = fmaf(wgt, x0[e], lc[e]); lc[4 + e] = fmaf(wgt, x1[e], lc[4 + e]); }
-    }
     bf16x8 hi, lo;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const bf16x2 h2 = to_bf16x2(ok ? lc[e] : 0.f, ok ? lc[e + 1] : 0.f);
-      const bf16x2 l2 = to_bf16x2(ok ? lc[e] - (float)h2[0] : 0.f, ok ? lc[e + 1] - (float)h2[1] : 0.f);
+      const bf16x2 h2 = to_bf16x2(ok ? lc[ks][e] : 0.f, ok ? lc[ks][e + 1] : 0.f);
+      const bf16x2 l2 = to_bf16x2(ok ? lc[ks][e] - (float)h2[0] : 0.f, ok ? lc[ks][e + 1] - (float)h2[1] : 0.f);
       hi[e] = h2[0]; hi[e + 1] = h2[1]; lo[e] = l2[0]; lo[e + 1] = l2[1];
     }
 #pragma unroll
