@@ -300,7 +300,11 @@ __device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* k2, c
 }
 
 // Segments of workgroup w: its contiguous unit range, cut at row-block
-// boundaries (see Plan).
+// boundaries (see Plan), visited last row block first.  A range that crosses
+// a boundary then starts at key tile 0, and its earlier row block's tail
+// follows at a fixed tile offset (the unit count per workgroup is nearly the
+// same for all), so the workgroups of one XCD sweep the cache nearly in step
+// and share its tiles in their L2 instead of each streaming the whole cache.
 struct SegmentIter {
   int64_t u, u_end;
   int T, rb_per_b;
@@ -309,15 +313,15 @@ struct SegmentIter {
   int64_t rb;
   int t0, t1, b, rbl;
   __device__ bool next() {
-    if (u >= u_end) return false;
-    rb = rb_of_unit(units, T, nrb, u);
+    if (u_end <= u) return false;
+    rb = rb_of_unit(units, T, nrb, u_end - 1);
     const int64_t first = rb_first_unit(units, T, rb);
-    const int64_t n_units = (units ? units[rb + 1] : first + T) - first;
-    t0 = (int)(u - first);
-    t1 = (int)min<int64_t>(n_units, (int64_t)t0 + (u_end - u));
+    const int64_t begin = max(u, first);
+    t0 = (int)(begin - first);
+    t1 = (int)(u_end - first);
     b = (int)(rb / rb_per_b);
     rbl = (int)(rb - (int64_t)b * rb_per_b);
-    u += (t1 - t0);
+    u_end = begin;
     return true;
   }
 };

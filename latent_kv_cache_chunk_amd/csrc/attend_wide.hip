@@ -322,18 +322,20 @@ void attend_wide_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstrid
   // visibility the last row blocks see the most keys, and starting the
   // longest ranges first keeps the tail of the launch short.
   const int64_t w = (int64_t)G - 1 - blockIdx.x;
-  int64_t u = unit_begin(w, U, G);
-  const int64_t u_end = unit_begin(w + 1, U, G);
+  const int64_t u = unit_begin(w, U, G);
+  int64_t u_end = unit_begin(w + 1, U, G);
   WaveState<DC, QB> st;
   if (blockIdx.x == 0 && threadIdx.x == 0) *hdr = PartitionHeader{U, G, units != nullptr ? 1 : 0};
 
   while (u < u_end) {
-    // this segment: the part of the range inside one row block (see Plan)
-    const int64_t rb = rb_of_unit(units, T, nrb, u);
+    // this segment: the part of the range inside one row block (see Plan),
+    // last row block first, so that ranges crossing a boundary start at key
+    // tile 0 and the workgroups of an XCD sweep the cache nearly in step
+    const int64_t rb = rb_of_unit(units, T, nrb, u_end - 1);
     const int64_t first = rb_first_unit(units, T, rb);
-    const int64_t n_units = (units ? units[rb + 1] : first + T) - first;
-    const int t0 = (int)(u - first);
-    const int t1 = (int)min<int64_t>(n_units, (int64_t)t0 + (u_end - u));
+    const int64_t begin = max(u, first);
+    const int t0 = (int)(begin - first);
+    const int t1 = (int)(u_end - first);
     const int b = (int)(rb / rb_per_b);
     const int rbl = (int)(rb - (int64_t)b * rb_per_b);
     const char* gbase = reinterpret_cast<const char*>(cache + (int64_t)b * cache_bstride);
@@ -394,7 +396,7 @@ void attend_wide_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstrid
         part_ml[(slot * kRowsPerBlock + rl) * 2 + 1] = l_tot;
       }
     }
-    u += (t1 - t0);
+    u_end = begin;
   }
 }
 
