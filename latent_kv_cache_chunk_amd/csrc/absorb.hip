@@ -12,54 +12,80 @@ namespace mla {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Rotation of every (query, rotary pair): cos and sin of the fp64 angle,
+// rounded to fp32 once; shared by all heads and batch samples.
+__global__ __launch_bounds__(256)
+void rope_table_kernel(const int* __restrict__ q_pos, int n_q, int pairs, RopeSpec rope, f32x2* __restrict__ cs) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n_q * pairs) return;
+  const int i = idx / pairs, pr = idx - i * pairs;
+  const double ang = rope_angle(pr, q_pos[3 * i], q_pos[3 * i + 1], q_pos[3 * i + 2], rope);
+  cs[idx] = f32x2{(float)cos(ang), (float)sin(ang)};
+}
+
 // One workgroup = 4 wavefronts = 128 queries of one (batch, head).
-// Content part on MFMA: C^T[c][i] = sum_d W_UK[h][d][c] q[i][d]; the A operand
-// (8 consecutive d of one column c) is gathered from global memory (W_UK is
-// small and L2 resident), the B operand is 16 contiguous bytes of q.
+// Content part on MFMA: C^T[c][i] = sum_d W_UK[h][d][c] q[i][d].  W_UK[h]
+// (128 x d_c) is staged once in LDS, rows padded to an odd number of 16-byte
+// slots, and its transpose is read as the A operand with ds_read_tr16_b64
+// (two reads give a lane eight d of one column c).  Those eight d are
+// {4h..4h+3, 8+4h..8+4h+3} of the 16-wide k-step for lane half h, so the B
+// operand takes q in the same order (two 8-byte loads).  The rotated
+// positional part comes from the (cos, sin) table.
 template <int DC>
 __global__ __launch_bounds__(256)
 void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
-                        const int* __restrict__ q_pos, int n_q, int H,
+                        const f32x2* __restrict__ rope_cs, int n_q, int H,
                         const u16* __restrict__ w_uk, float qscale,
-                        u16* __restrict__ qt, int rows_pad_b, RopeSpec rope) {
+                        u16* __restrict__ qt, int rows_pad_b) {
   constexpr int DH = 128, DR = 32, W = DC + DR, CB = DC / 32;
+  constexpr int NCH = DC / 8, ROWB = (NCH + 1) * 16;
+  static_assert((NCH + 1) & 1, "odd slot stride");
+  __shared__ __attribute__((aligned(16))) char wl[DH * ROWB];
   const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
   const int i = blockIdx.y * 128 + wave * 32 + (lane & 31);
   const bool ok = i < n_q;
-  const int64_t qrow_off = (((int64_t)b * n_q + (ok ? i : 0)) * H + h);
-  const u16* qrow = q + qrow_off * DH + half * 8;
-
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  bf16x8 qf[DH / 16];
-#pragma unroll
-  for (int ks = 0; ks < DH / 16; ++ks)
-    qf[ks] = ok ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16) : __builtin_bit_cast(bf16x8, zero);
 
   const u16* wk = w_uk + (int64_t)h * DH * DC;
-  u16* orow = qt + ((int64_t)b * rows_pad_b + (int64_t)h * n_q + i) * W;
+  for (int idx = threadIdx.x; idx < DH * NCH; idx += 256) {
+    const int r = idx / NCH, ch = idx - r * NCH;
+    *reinterpret_cast<uint4*>(wl + r * ROWB + ch * 16) = *reinterpret_cast<const uint4*>(wk + r * DC + ch * 8);
+  }
 
+  const int64_t qrow_off = (((int64_t)b * n_q + (ok ? i : 0)) * H + h);
+  const u16* qrow = q + qrow_off * DH + half * 4;
+  bf16x8 qf[DH / 16];
+#pragma unroll
+  for (int ks = 0; ks < DH / 16; ++ks) {
+    const uint2 lo = ok ? *reinterpret_cast<const uint2*>(qrow + ks * 16) : make_uint2(0, 0);
+    const uint2 hi = ok ? *reinterpret_cast<const uint2*>(qrow + ks * 16 + 8) : make_uint2(0, 0);
+    qf[ks] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+  }
+  __syncthreads();
+
+  const int g = lane >> 4, j = lane & 15;
+  const char* abase = wl + ((g >> 1) * 4 + (j >> 2)) * ROWB + (16 * (g & 1) + 4 * (j & 3)) * 2;
+  u16* orow = qt + ((int64_t)b * rows_pad_b + (int64_t)h * n_q + i) * W;
 #pragma unroll 1
   for (int cb = 0; cb < CB; ++cb) {
-    const int c = cb * 32 + (lane & 31);
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks) {
-      const u16* col = wk + (int64_t)(ks * 16 + half * 8) * DC + c;
-      u16 e8[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) e8[e] = col[(int64_t)e * DC];
-      bf16x8 a;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] = __builtin_bit_cast(__bf16, e8[e]);
+      const char* ab = abase + ks * 16 * ROWB + cb * 64;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)ab);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ab + 8 * ROWB));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       acc = mfma_32x32x16(a, qf[ks], acc);
     }
     if (ok) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c0 = cb * 32 + g * 8 + half * 4;
-        const uint32_t lo = bf16x2_bits(to_bf16x2(acc[4 * g] * qscale, acc[4 * g + 1] * qscale));
-        const uint32_t hi = bf16x2_bits(to_bf16x2(acc[4 * g + 2] * qscale, acc[4 * g + 3] * qscale));
+      for (int gg = 0; gg < 4; ++gg) {
+        const int c0 = cb * 32 + gg * 8 + half * 4;
+        const uint32_t lo = bf16x2_bits(to_bf16x2(acc[4 * gg] * qscale, acc[4 * gg + 1] * qscale));
+        const uint32_t hi = bf16x2_bits(to_bf16x2(acc[4 * gg + 2] * qscale, acc[4 * gg + 3] * qscale));
         *reinterpret_cast<uint2*>(orow + c0) = make_uint2(lo, hi);
       }
     }
@@ -68,15 +94,14 @@ void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
   // Positional part: lane half `half` rotates pairs 8*half .. 8*half+7.
   if (ok) {
     const u16* qr = q_r + qrow_off * DR + half * 16;
-    const int pt = q_pos[3 * i], ph = q_pos[3 * i + 1], pw = q_pos[3 * i + 2];
+    const f32x2* cs = rope_cs + (int64_t)i * (DR / 2) + half * 8;
     uint32_t outw[8];
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
       const float x0 = (float)__builtin_bit_cast(__bf16, qr[2 * pp]);
       const float x1 = (float)__builtin_bit_cast(__bf16, qr[2 * pp + 1]);
-      const double ang = rope_angle(half * 8 + pp, pt, ph, pw, rope);
-      const float cs = (float)cos(ang), sn = (float)sin(ang);
-      const float y0 = fmaf(x0, cs, -(x1 * sn)), y1 = fmaf(x0, sn, x1 * cs);
+      const f32x2 r = cs[pp];
+      const float y0 = fmaf(x0, r[0], -(x1 * r[1])), y1 = fmaf(x0, r[1], x1 * r[0]);
       outw[pp] = bf16x2_bits(to_bf16x2(y0 * qscale, y1 * qscale));
     }
     uint4* o = reinterpret_cast<uint4*>(orow + DC + half * 16);
@@ -138,16 +163,20 @@ void absorb_f32_kernel(const float* __restrict__ q, const float* __restrict__ q_
 }
 
 hipError_t launch_absorb_bf16(const Plan& p, const AbsorbArgs& a, hipStream_t s) {
+  const int pairs = (p.width - p.d_c) / 2;
+  f32x2* cs = (f32x2*)a.rope_cs;
+  rope_table_kernel<<<dim3((unsigned)((p.n_q * pairs + 255) / 256)), dim3(256), 0, s>>>(a.q_pos, p.n_q, pairs, a.rope,
+                                                                                         cs);
   const dim3 grid(p.B * p.H, (p.n_q + 127) / 128), block(256);
   const u16* q = (const u16*)a.q;
   const u16* qr = (const u16*)a.q_r;
   const u16* wk = (const u16*)a.w_uk;
   u16* qt = (u16*)a.qt;
   switch (p.d_c) {
-    case 64: absorb_bf16_kernel<64><<<grid, block, 0, s>>>(q, qr, a.q_pos, p.n_q, p.H, wk, a.qscale, qt, p.rows_pad_b, a.rope); break;
-    case 128: absorb_bf16_kernel<128><<<grid, block, 0, s>>>(q, qr, a.q_pos, p.n_q, p.H, wk, a.qscale, qt, p.rows_pad_b, a.rope); break;
-    case 192: absorb_bf16_kernel<192><<<grid, block, 0, s>>>(q, qr, a.q_pos, p.n_q, p.H, wk, a.qscale, qt, p.rows_pad_b, a.rope); break;
-    case 256: absorb_bf16_kernel<256><<<grid, block, 0, s>>>(q, qr, a.q_pos, p.n_q, p.H, wk, a.qscale, qt, p.rows_pad_b, a.rope); break;
+    case 64: absorb_bf16_kernel<64><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, wk, a.qscale, qt, p.rows_pad_b); break;
+    case 128: absorb_bf16_kernel<128><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, wk, a.qscale, qt, p.rows_pad_b); break;
+    case 192: absorb_bf16_kernel<192><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, wk, a.qscale, qt, p.rows_pad_b); break;
+    case 256: absorb_bf16_kernel<256><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, wk, a.qscale, qt, p.rows_pad_b); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -109,6 +109,7 @@ int32_t do_absorb(const mla_dims* d, int32_t dtype, const mla::Plan& p, const vo
   a.q = q; a.q_r = q_r; a.q_pos = q_pos; a.w_uk = w_uk;
   a.qscale = (float)((double)scale * mla::kLog2e);
   a.qt = (char*)ws + p.off_qt;
+  a.rope_cs = (char*)ws + p.off_rope;
   a.rope = rope_of(d);
   hipError_t e = dtype == MLA_BF16 ? mla::launch_absorb_bf16(p, a, s) : mla::launch_absorb_f32(p, a, s);
   return finish(e, s, "mla_query_absorb");

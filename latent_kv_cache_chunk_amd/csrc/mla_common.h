@@ -79,7 +79,7 @@ struct Plan {
   bool causal;          // per-row-block units (chunk-causal call)
   int32_t elem;         // bytes per element of q~ (2 bf16, 4 f32)
   // byte offsets inside the workspace
-  int64_t off_qt, off_L, off_ml, off_units, off_hdr, total;
+  int64_t off_qt, off_L, off_ml, off_units, off_hdr, off_rope, total;
 };
 
 // The partition the attention kernel used, left in the workspace for the merge.
@@ -158,7 +158,8 @@ inline Plan make_plan(int B, int H, int n_q, int n_k, int d_c, int d_r, bool f32
   int64_t ml_bytes = slots * kRowsPerBlock * 2 * 4;
   p.off_units = align_up(p.off_ml + ml_bytes, 256);
   p.off_hdr = align_up(p.off_units + (int64_t)(p.nrb + 1) * 8, 256);
-  p.total = align_up(p.off_hdr + (int64_t)sizeof(PartitionHeader), 256);
+  p.off_rope = align_up(p.off_hdr + (int64_t)sizeof(PartitionHeader), 256);   // (cos, sin) per query and pair
+  p.total = align_up(p.off_rope + (int64_t)n_q * (d_r / 2) * 8, 256);
   return p;
 }
 

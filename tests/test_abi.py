@@ -90,8 +90,9 @@ def test_workspace_plan_sizes():
     slots = 256 + 220
     states = slots * 256 * (192 + 2) * 4
     units = (220 + 1) * 8
-    assert n480 >= qt + states + units
-    assert n480 < qt + states + units + 4096
+    rope = 4680 * 16 * 8                     # (cos, sin) per query and rotary pair, fp32
+    assert n480 >= qt + states + units + rope
+    assert n480 < qt + states + units + rope + 4096
     # fp32 variant: one slot per row-block
     n32 = _ws(d, 1, 48, 192)
     assert n32 >= 3 * 256 * 224 * 4 + 3 * 256 * 194 * 4
