@@ -282,14 +282,17 @@ template <int DQK, bool SCORE>
 __device__ __forceinline__ void role(Ctx& c, const Problem& pr, int64_t w, char* k0, char* k1, char* v0, char* v1,
                                      char* pb0, char* pb1) {
   using L = Tile<DQK>;
-  int64_t u = unit_begin(w, pr.U, pr.G);
-  const int64_t u_end = unit_begin(w + 1, pr.U, pr.G);
+  // segments last row block first (see the latent attention kernel): a range
+  // that crosses a row-block boundary starts at key tile 0
+  const int64_t u = unit_begin(w, pr.U, pr.G);
+  int64_t u_end = unit_begin(w + 1, pr.U, pr.G);
   ScoreState<DQK> ss;
   ValueState vs;
   while (u < u_end) {
-    const int64_t rb = u / pr.T;
-    const int t0 = (int)(u - rb * pr.T);
-    const int t1 = (int)min<int64_t>(pr.T, (int64_t)t0 + (u_end - u));
+    const int64_t rb = (u_end - 1) / pr.T;
+    const int64_t begin = max(u, rb * pr.T);
+    const int t0 = (int)(begin - rb * pr.T);
+    const int t1 = (int)(u_end - rb * pr.T);
     begin_segment<DQK>(c, pr, rb);
     const int64_t bh = rb / pr.rb_per_bh;
     const int rbl = (int)(rb - bh * pr.rb_per_bh);
@@ -359,7 +362,7 @@ __device__ __forceinline__ void role(Ctx& c, const Problem& pr, int64_t w, char*
           }
       }
     }
-    u += (t1 - t0);
+    u_end = begin;
   }
 }
 
