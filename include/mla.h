@@ -128,7 +128,8 @@ int64_t mla_chunk_attend_workspace_bytes(const mla_dims* dims, int32_t dtype,
  *   out      device [B, n_q, H, d_h] of out_dtype
  *   workspace device, at least mla_chunk_attend_workspace_bytes(...) bytes;
  *            its contents on entry are irrelevant and on exit unspecified.
- * Requires 1 <= n_q <= n_k <= cache_capacity. */
+ * Requires 1 <= n_q <= n_k <= cache_capacity and, for bf16, n_k * (d_c + d_r) * 2 < 2^32
+ * (one sample's visible keys below 4 GiB; MLA_ERR_UNSUPPORTED otherwise). */
 int32_t mla_chunk_attend(const mla_dims* dims, int32_t in_dtype, int32_t out_dtype,
                          const void* q, const void* q_r, const int32_t* q_pos, int32_t n_q,
                          const void* w_uk, const void* w_uv,

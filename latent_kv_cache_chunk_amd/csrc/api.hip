@@ -91,6 +91,9 @@ int32_t check_attend_sizes(const mla_dims* d, int32_t dtype, int32_t n_q, int32_
   if ((int64_t)d->n_heads * n_q > (int64_t)1 << 30) return fail(MLA_ERR_UNSUPPORTED, "n_heads * n_q too large");
   if ((int64_t)d->batch * ((int64_t)d->n_heads * n_q + 255) / 256 > (int64_t)1 << 24)
     return fail(MLA_ERR_UNSUPPORTED, "batch * rows too large");
+  // the attention kernels address a sample's keys with 32-bit byte offsets
+  if (dtype == MLA_BF16 && (int64_t)n_k * (d->d_c + d->d_r) * 2 >= (int64_t)1 << 32)
+    return fail(MLA_ERR_UNSUPPORTED, "n_k (%d) too large: one sample's keys must stay below 4 GiB", n_k);
   *plan = mla::make_plan(d->batch, d->n_heads, n_q, n_k, d->d_c, d->d_r, dtype == MLA_F32);
   return MLA_OK;
 }

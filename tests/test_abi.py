@@ -157,6 +157,16 @@ def test_causal_validation():
                                         ctypes.byref(mla.MlaCausal(144, 0)), fake, 1 << 40, None) == -1
 
 
+def test_key_count_limit_of_32_bit_offsets():
+    lib = mla.raw()
+    d = _dims()                                          # d_c + d_r = 224: 448 bytes per key
+    limit = (1 << 32) // 448
+    assert lib.mla_chunk_attend_workspace_bytes(ctypes.byref(d), 0, 48, limit) > 0
+    assert lib.mla_chunk_attend_workspace_bytes(ctypes.byref(d), 0, 48, limit + 1) == -2
+    assert b"4 GiB" in lib.mla_last_error()
+    assert lib.mla_chunk_attend_workspace_bytes(ctypes.byref(d), 1, 48, limit + 1) > 0   # fp32 kernels use 64-bit offsets
+
+
 def test_mha_validation_and_workspace():
     lib = mla.raw()
     fake = ctypes.c_void_p(0x10000)
