@@ -565,6 +565,7 @@ MhaPlan make_mha_plan(int B, int H, int n_q, int n_k, int dqk, bool expanded) {
   const int64_t rounds = (p.nrb + kPartitionCUs - 1) / kPartitionCUs;
   if ((double)p.nrb / (double)(rounds * kPartitionCUs) < 0.9) G = rounds * kPartitionCUs;
   if (G > p.U) G = p.U;
+  if (G > p.nrb * kMaxSplitsPerBlock) G = p.nrb * kMaxSplitsPerBlock;
   p.G = (int32_t)G;
   const int64_t slots = G + p.nrb;
   p.off_qt = 0;

@@ -23,6 +23,10 @@ constexpr int kRowsPerBlock = 256;
 __host__ __device__ constexpr int key_tile(int d_c) { return d_c <= 192 ? 64 : 128; }
 // Compute units the work partition is sized for (MI355X).
 constexpr int kPartitionCUs = 256;
+// Most workgroups that share one row block.  Short chunks (few row blocks)
+// would otherwise spread each row block over up to a hundred workgroups and
+// leave the merge that many partial states per row.
+constexpr int kMaxSplitsPerBlock = 16;
 // log2(e): softmax runs in base 2 with this folded into the query scale.
 constexpr double kLog2e = 1.4426950408889634074;
 
@@ -118,8 +122,9 @@ inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 // Build the plan.  bf16: stream-K style partition over kPartitionCUs when the
 // plain one-workgroup-per-row-block launch would leave more than 10% of the
 // compute units idle in its last round; chunk-causal calls always spread
-// their (uneven) units over kPartitionCUs workgroups.  f32: one workgroup per
-// row-block.  The workspace size does not depend on `vis`.
+// their (uneven) units over kPartitionCUs workgroups; either way no row block
+// is split over more than kMaxSplitsPerBlock workgroups.  f32: one workgroup
+// per row-block.  The workspace size does not depend on `vis`.
 inline Plan make_plan(int B, int H, int n_q, int n_k, int d_c, int d_r, bool f32,
                       const Visibility* vis = nullptr) {
   Plan p{};
@@ -138,6 +143,7 @@ inline Plan make_plan(int B, int H, int n_q, int n_k, int d_c, int d_r, bool f32
     double eff = (double)p.nrb / (double)(rounds * kPartitionCUs);
     if (eff < 0.9) G = rounds * kPartitionCUs;
     if (G > p.U) G = p.U;
+    if (G > (int64_t)p.nrb * kMaxSplitsPerBlock) G = (int64_t)p.nrb * kMaxSplitsPerBlock;
   }
   const int64_t g_slots = G > kPartitionCUs ? G : kPartitionCUs;   // covers the chunk-causal G too
   if (!f32 && vis != nullptr && vis->chunk_len != 0) {
@@ -146,6 +152,7 @@ inline Plan make_plan(int B, int H, int n_q, int n_k, int d_c, int d_r, bool f32
       per_b += (vis->kv_max_of_block(rbl * kRowsPerBlock, n_k) + bn - 1) / bn;
     p.U = (int64_t)B * per_b;
     G = p.U < kPartitionCUs ? p.U : kPartitionCUs;
+    if (G > (int64_t)p.nrb * kMaxSplitsPerBlock) G = (int64_t)p.nrb * kMaxSplitsPerBlock;
     p.causal = true;
   }
   p.G = (int32_t)G;

@@ -22,6 +22,7 @@ void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restric
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
   const int i = blockIdx.y * 128 + wave * 32 + (lane & 31);
   const bool ok = i < n_q;
+  if (blockIdx.y * 128 + wave * 32 >= n_q) return;   // no real row in this wavefront (no barriers follow)
   const int r = h * n_q + (ok ? i : 0);
   const int64_t rb = (int64_t)b * rb_per_b + r / kRowsPerBlock;
   const int rl = r % kRowsPerBlock;
