@@ -232,6 +232,29 @@ int32_t mla_chunk_attend_expanded(const mla_dims* dims, int32_t out_dtype,
                                   float softmax_scale, void* out,
                                   void* workspace, int64_t workspace_bytes, void* stream);
 
+/* The faster of the two evaluation orders for a chunk step's shape, picked
+ * from measured times on MI355X: MLA_FORM_EXPANDED (mla_chunk_attend_expanded)
+ * when in_dtype is MLA_BF16, d_c >= 192 and n_q >= 2048 (and the per-head keys
+ * fit its limits); otherwise MLA_FORM_ABSORBED (mla_chunk_attend).  At the 480P shape (d_c = 192, 4680
+ * queries, 32760 keys) the non-absorbed form is about 15% faster; below about
+ * 1560 queries, or at d_c <= 128, the absorbed form is.  Negative mla_status
+ * on arguments mla_chunk_attend would reject. */
+enum { MLA_FORM_ABSORBED = 0, MLA_FORM_EXPANDED = 1 };
+int32_t mla_chunk_attend_form(const mla_dims* dims, int32_t in_dtype, int32_t n_q, int32_t n_k);
+
+/* Workspace bytes of mla_chunk_attend_auto: those of the form it picks. */
+int64_t mla_chunk_attend_auto_workspace_bytes(const mla_dims* dims, int32_t in_dtype, int32_t n_q, int32_t n_k);
+
+/* mla_chunk_attend through the form mla_chunk_attend_form picks (the same
+ * function up to rounding); arguments and errors as for mla_chunk_attend,
+ * with a workspace of at least mla_chunk_attend_auto_workspace_bytes. */
+int32_t mla_chunk_attend_auto(const mla_dims* dims, int32_t in_dtype, int32_t out_dtype,
+                              const void* q, const void* q_r, const int32_t* q_pos, int32_t n_q,
+                              const void* w_uk, const void* w_uv,
+                              const void* cache, int32_t cache_capacity, int32_t n_k,
+                              float softmax_scale, void* out,
+                              void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Rolling latent cache for long rollouts (a fixed-size sliding window of
  * cached chunks: VideoMLA arXiv abstract), with `sink_chunks` leading
  * chunks kept for the whole rollout.  Host-side bookkeeping only; the cache

@@ -415,6 +415,40 @@ int32_t mla_chunk_attend_causal(const mla_dims* dims, int32_t in_dtype, int32_t 
                            causal, softmax_scale, out, workspace, workspace_bytes, stream);
 }
 
+int32_t mla_chunk_attend_form(const mla_dims* dims, int32_t in_dtype, int32_t n_q, int32_t n_k) {
+  mla::Plan p;
+  int32_t st = check_attend_sizes(dims, in_dtype, n_q, n_k, &p);
+  if (st) return st;
+  // Thresholds from timing both forms on MI355X (n_k = 32760; d_c 64-256):
+  // the non-absorbed form wins from d_c = 192 on once a chunk has about 2048
+  // queries (padding each head's rows to 256 then adds at most an eighth).
+  if (in_dtype != MLA_BF16 || dims->d_c < 192 || n_q < 2048) return MLA_FORM_ABSORBED;
+  if (check_mha_sizes(dims->batch, dims->n_heads, n_q, n_k, 160) ||
+      (int64_t)n_k * dims->n_heads * 160 * 2 >= (int64_t)1 << 32)
+    return MLA_FORM_ABSORBED;
+  return MLA_FORM_EXPANDED;
+}
+
+int64_t mla_chunk_attend_auto_workspace_bytes(const mla_dims* dims, int32_t in_dtype, int32_t n_q, int32_t n_k) {
+  const int32_t form = mla_chunk_attend_form(dims, in_dtype, n_q, n_k);
+  if (form < 0) return form;
+  return form == MLA_FORM_EXPANDED ? mla_chunk_attend_expanded_workspace_bytes(dims, n_q, n_k)
+                                   : mla_chunk_attend_workspace_bytes(dims, in_dtype, n_q, n_k);
+}
+
+int32_t mla_chunk_attend_auto(const mla_dims* dims, int32_t in_dtype, int32_t out_dtype, const void* q,
+                              const void* q_r, const int32_t* q_pos, int32_t n_q, const void* w_uk, const void* w_uv,
+                              const void* cache, int32_t cache_capacity, int32_t n_k, float softmax_scale, void* out,
+                              void* workspace, int64_t workspace_bytes, void* stream) {
+  const int32_t form = mla_chunk_attend_form(dims, in_dtype, n_q, n_k);
+  if (form < 0) return form;
+  if (form == MLA_FORM_EXPANDED)
+    return mla_chunk_attend_expanded(dims, out_dtype, q, q_r, q_pos, n_q, w_uk, w_uv, cache, cache_capacity, n_k,
+                                     softmax_scale, out, workspace, workspace_bytes, stream);
+  return chunk_attend_impl(dims, in_dtype, out_dtype, q, q_r, q_pos, n_q, w_uk, w_uv, cache, cache_capacity, n_k,
+                           nullptr, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
 const char* mla_status_string(int32_t status) {
   switch (status) {
     case MLA_OK: return "MLA_OK";

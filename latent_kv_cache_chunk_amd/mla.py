@@ -31,7 +31,8 @@ EXPORTED = ("mla_cache_append", "mla_chunk_attend_workspace_bytes", "mla_chunk_a
             "mla_ring_init", "mla_ring_current", "mla_ring_commit", "mla_ring_slot_chunks",
             "mla_cache_bytes", "mla_dense_kv_bytes", "mla_ring_last_error",
             "mla_mha_attend_workspace_bytes", "mla_mha_attend",
-            "mla_chunk_attend_expanded_workspace_bytes", "mla_chunk_attend_expanded")
+            "mla_chunk_attend_expanded_workspace_bytes", "mla_chunk_attend_expanded",
+            "mla_chunk_attend_form", "mla_chunk_attend_auto_workspace_bytes", "mla_chunk_attend_auto")
 
 
 class MlaDims(ctypes.Structure):
@@ -84,6 +85,13 @@ _lib.mla_chunk_attend_expanded_workspace_bytes.restype = _I64
 _lib.mla_chunk_attend_expanded.argtypes = [_DIMS, _I32, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, ctypes.c_float,
                                            _P, _P, _I64, _P]
 _lib.mla_chunk_attend_expanded.restype = _I32
+
+_lib.mla_chunk_attend_form.argtypes = [_DIMS, _I32, _I32, _I32]
+_lib.mla_chunk_attend_form.restype = _I32
+_lib.mla_chunk_attend_auto_workspace_bytes.argtypes = [_DIMS, _I32, _I32, _I32]
+_lib.mla_chunk_attend_auto_workspace_bytes.restype = _I64
+_lib.mla_chunk_attend_auto.argtypes = list(_lib.mla_chunk_attend.argtypes)
+_lib.mla_chunk_attend_auto.restype = _I32
 
 _lib.mla_ring_init.argtypes = [_RING, _I32, _I32, _I32]
 _lib.mla_ring_init.restype = _I32
@@ -326,6 +334,40 @@ def chunk_attend_expanded(dims: Dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k: int
                                           cache.shape[1], int(n_k), float(scale), out.data_ptr(),
                                           workspace.data_ptr(), workspace.numel(), _stream(stream))
     _raise(code, "mla_chunk_attend_expanded")
+    return out
+
+
+MLA_FORM_ABSORBED, MLA_FORM_EXPANDED = 0, 1
+
+
+def chunk_attend_form(dims: Dims, dtype: torch.dtype, n_q: int, n_k: int) -> int:
+    """MLA_FORM_ABSORBED or MLA_FORM_EXPANDED: the form mla_chunk_attend_auto runs for this shape."""
+    d = dims.c()
+    f = _lib.mla_chunk_attend_form(ctypes.byref(d), _dtype_code(dtype), int(n_q), int(n_k))
+    if f < 0:
+        _raise(int(f), "mla_chunk_attend_form")
+    return int(f)
+
+
+def chunk_attend_auto(dims: Dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k: int, scale: float,
+                      out=None, out_dtype=None, workspace=None, stream=None) -> torch.Tensor:
+    """chunk_attend through the faster evaluation order for the shape (mla_chunk_attend_auto)."""
+    n_q, dt = _attend_checks(dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k)
+    odt = dt if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((dims.batch, n_q, dims.n_heads, dims.head_dim), dtype=odt, device=q.device)
+    _check(out, "out", (dims.batch, n_q, dims.n_heads, dims.head_dim), odt)
+    d = dims.c()
+    if workspace is None:
+        n = _lib.mla_chunk_attend_auto_workspace_bytes(ctypes.byref(d), _dtype_code(dt), n_q, int(n_k))
+        if n < 0:
+            _raise(int(n), "mla_chunk_attend_auto_workspace_bytes")
+        workspace = torch.empty(int(n), dtype=torch.uint8, device=q.device)
+    code = _lib.mla_chunk_attend_auto(ctypes.byref(d), _dtype_code(dt), _dtype_code(odt), q.data_ptr(),
+                                      q_r.data_ptr(), q_pos.data_ptr(), n_q, w_uk.data_ptr(), w_uv.data_ptr(),
+                                      cache.data_ptr(), cache.shape[1], int(n_k), float(scale), out.data_ptr(),
+                                      workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _raise(code, "mla_chunk_attend_auto")
     return out
 
 

@@ -203,6 +203,25 @@ def test_mha_validation_and_workspace():
     assert expanded(ws_bytes=4096) == -3
 
 
+def test_chunk_attend_form_rule():
+    lib = mla.raw()
+    form = lambda d, dt, n_q, n_k=32760: lib.mla_chunk_attend_form(ctypes.byref(d), dt, n_q, n_k)
+    d192 = _dims()
+    assert form(d192, 0, 4680) == 1                     # 480P chunk: non-absorbed (4864 rows per head)
+    assert form(d192, 0, 3120) == 1
+    assert form(d192, 0, 1560) == 0                     # below 2048 queries
+    assert form(d192, 0, 2047) == 0
+    assert form(d192, 0, 2048) == 1
+    assert form(d192, 1, 4680) == 0                     # fp32 inputs: absorbed only
+    assert form(_dims(d_c=128), 0, 4680) == 0
+    assert form(_dims(d_c=256), 0, 4680) == 1
+    assert form(d192, 0, 0) == -1                       # arguments mla_chunk_attend rejects
+    ws_auto = lib.mla_chunk_attend_auto_workspace_bytes(ctypes.byref(d192), 0, 4680, 32760)
+    assert ws_auto == lib.mla_chunk_attend_expanded_workspace_bytes(ctypes.byref(d192), 4680, 32760)
+    assert lib.mla_chunk_attend_auto_workspace_bytes(ctypes.byref(d192), 0, 48, 192) == \
+        lib.mla_chunk_attend_workspace_bytes(ctypes.byref(d192), 0, 48, 192)
+
+
 def test_binding_checks_tensors_on_host():
     d = mla.Dims(batch=1)
     with pytest.raises(ValueError):

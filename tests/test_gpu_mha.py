@@ -164,3 +164,38 @@ def test_expanded_480p_sampled_rows():
                                     np64(inp["w_uv"]), np64(inp["cache"]), wl.n_k, wl.scale)
     assert_g2(got[rows[:, 0], rows[:, 1], rows[:, 2]], want, "480p expanded")
     assert np.all(np.isfinite(got))
+
+
+# ----------------------------------------------------------------- per-shape choice of the form
+
+def test_auto_short_chunk_runs_the_absorbed_form():
+    mla = need_gpu()
+    wl = synth.TINY
+    inp = synth.attend_inputs(wl, seed=4)
+    assert mla.chunk_attend_form(_dims(mla, wl), torch.bfloat16, wl.n_q, wl.n_k) == mla.MLA_FORM_ABSORBED
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    args = (_dims(mla, wl), d["q"], d["q_r"], d["q_pos"], d["w_uk"], d["w_uv"], d["cache"], wl.n_k, wl.scale)
+    a = mla.chunk_attend(*args, out_dtype=torch.float32)
+    b = mla.chunk_attend_auto(*args, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_auto_long_chunk_runs_the_non_absorbed_form():
+    """2048 queries (16 x 32 tokens per frame, 4 frames) over 3072 keys: the expanded form."""
+    mla = need_gpu()
+    wl = replace(synth.TINY, name="auto_long", grid_hw=(16, 32), cache_frames=(0, 1), query_frames=(2, 3, 4, 5))
+    assert (wl.n_q, wl.n_k) == (2048, 3072)
+    assert mla.chunk_attend_form(_dims(mla, wl), torch.bfloat16, wl.n_q, wl.n_k) == mla.MLA_FORM_EXPANDED
+    inp = synth.attend_inputs(wl, seed=5)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    args = (_dims(mla, wl), d["q"], d["q_r"], d["q_pos"], d["w_uk"], d["w_uv"], d["cache"], wl.n_k, wl.scale)
+    a = mla.chunk_attend_expanded(*args, out_dtype=torch.float32)
+    b = mla.chunk_attend_auto(*args, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    rng = np.random.default_rng(8)
+    rows = np.stack([np.zeros(40, np.int64), rng.integers(0, wl.n_q, 40), rng.integers(0, wl.n_heads, 40)], 1)
+    want = oracle.chunk_attend_rows(rows, np64(inp["q"]), np64(inp["q_r"]), inp["q_pos"].numpy(), np64(inp["w_uk"]),
+                                    np64(inp["w_uv"]), np64(inp["cache"]), wl.n_k, wl.scale)
+    assert_g2(np64(b)[rows[:, 0], rows[:, 1], rows[:, 2]], want, "auto long")
