@@ -508,6 +508,7 @@ void mha_uplift_kernel(const u16* __restrict__ cache, int64_t cap, int n_k, int 
                        u16* __restrict__ K, u16* __restrict__ V) {
   constexpr int W = DC + 32, DH = 128, DQK = DH + 32, KS = DC / 16, WROW = DC * 2 + 16, CPR = DC / 8;
   __shared__ __attribute__((aligned(16))) char wt[DH * WROW];
+  __shared__ __attribute__((aligned(16))) char stage[8][32 * 64];   // per wavefront: 32 tokens x 32 outputs
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
   const int h = blockIdx.y;
   const bool is_v = blockIdx.z != 0;
@@ -526,6 +527,19 @@ void mha_uplift_kernel(const u16* __restrict__ cache, int64_t cap, int n_k, int 
   const int64_t kv_row = ((int64_t)b * n_k + j) * H + h;
   u16* dst = is_v ? V + kv_row * DH : K + kv_row * DQK;
   const bool live = tok < ntok;
+  // the rows this lane stores from the staging area: token (lane >> 2) + 16u, 16-byte piece (lane & 3)
+  char* st = stage[wave];
+  u16* sdst[2];
+  bool slive[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = tok - (lane & 31) + (lane >> 2) + 16 * u;   // token of the wavefront's 32
+    slive[u] = t < ntok;
+    const int tt = min(t, ntok - 1);
+    const int tb = tt / n_k, tj = tt - tb * n_k;
+    const int64_t row = ((int64_t)tb * n_k + tj) * H + h;
+    sdst[u] = (is_v ? V + row * DH : K + row * DQK) + (lane & 3) * 8;
+  }
   __syncthreads();
 #pragma unroll 1
   for (int ob = 0; ob < 4; ++ob) {
@@ -533,13 +547,17 @@ void mha_uplift_kernel(const u16* __restrict__ cache, int64_t cap, int n_k, int 
     f32x16 acc = {};
 #pragma unroll
     for (int k = 0; k < KS; ++k) acc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(a + k * 32), cf[k], acc);
-    // lane holds its token's outputs 32*ob + 8g + 4*half + t, t = 0..3
-    if (live) {
+    // lane holds its token's outputs 32*ob + 8g + 4*half + t, t = 0..3: stage them, then store
+    // each token's 64 bytes of this block as four 16-byte pieces from four lanes
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<uint2*>(dst + ob * 32 + g * 8 + half * 4) =
-            make_uint2(bf16x2_bits(to_bf16x2(acc[4 * g], acc[4 * g + 1])),
-                       bf16x2_bits(to_bf16x2(acc[4 * g + 2], acc[4 * g + 3])));
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<uint2*>(st + (lane & 31) * 64 + (g * 8 + half * 4) * 2) =
+          make_uint2(bf16x2_bits(to_bf16x2(acc[4 * g], acc[4 * g + 1])),
+                     bf16x2_bits(to_bf16x2(acc[4 * g + 2], acc[4 * g + 3])));
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint4 piece = *reinterpret_cast<const uint4*>(st + ((lane >> 2) + 16 * u) * 64 + (lane & 3) * 16);
+      if (slive[u]) *reinterpret_cast<uint4*>(sdst[u] + ob * 32) = piece;
     }
   }
   if (!is_v && live) {   // the positional key, shared by every head
