@@ -72,7 +72,7 @@ struct AttendTile {
   static constexpr int TILEB = BN * ROWB;    // LDS bytes per key buffer
   static constexpr int ROWS_PER_LOAD = 64 / NSLOT;   // whole rows one 64-lane load copies
   static constexpr int NLOAD = (BN + ROWS_PER_LOAD - 1) / ROWS_PER_LOAD;
-  static constexpr int LOADS_PER_WAVE = (NLOAD + kWaves - 1) / kWaves;
+  static constexpr int LOADS_PER_WAVE = (NLOAD + kGroups - 1) / kGroups;   // value wavefronts issue the loads
   static constexpr int KS = W / 16;          // score k-steps
   static constexpr int CB = DC / 32;         // 32-column latent blocks of O^T
   static constexpr int PBLK = kGroups * 2 * 2 * 64 * 16;   // P bytes of one block: groups x halves x k-steps x lanes
@@ -105,8 +105,11 @@ struct SweepCtx {
   int v_off;           // transposed latent operand offset inside a block
 };
 
-// Enqueue this wavefront's share of the direct-to-LDS loads of key tile t
-// into `tile`.  Load i copies R = ROWS_PER_LOAD whole rows, [iR, iR + R), to
+// Enqueue this value wavefront's share of the direct-to-LDS loads of key tile
+// t into `tile`.  Only the value wavefronts issue loads: the score wavefront
+// is each step's critical path (its scores, softmax and P stores take longer
+// than the value product), and the loads' issue costs it about 300 cycles a
+// step.  Load i copies R = ROWS_PER_LOAD whole rows, [iR, iR + R), to
 // LDS rows [iR, iR + R); in the last, partial tile rows past n_k re-read key
 // n_k-1 (their scores are masked).  Source addresses are the sample's base
 // plus a 32-bit unsigned offset (a sample's cache is below 4 GiB).
@@ -116,7 +119,7 @@ __device__ inline void issue_tile(const SweepCtx& c, int t, char* tile) {
   const int key0 = t * L::BN;
 #pragma unroll
   for (int i = 0; i < L::LOADS_PER_WAVE; ++i) {
-    const int ld = c.wave + kWaves * i;
+    const int ld = c.group + kGroups * i;
     if (ld < L::NLOAD) {
       const int row0 = ld * L::ROWS_PER_LOAD;
       const uint32_t key = (uint32_t)min(key0 + row0 + c.lane_row, c.n_k - 1);
@@ -262,14 +265,14 @@ __device__ __forceinline__ void value_tile(ValueState<DC>& st, const char* tile,
 }
 
 // ------------------------------------------------------------------ sweeps
-// One step of a segment's sweep: start tile k+1 into `nxt`, do this role's
+// One step of a segment's sweep: (value wavefronts) start tile k+1 into `nxt`, do this role's
 // work (score: tile k in `cur`, P to P[k % 2]; value: tile k-1 in `prv`, P
 // from P[(k-1) % 2]), then wait for the loads and barrier.  Steps run
 // k = 0 .. n (n tiles); returns true after step n.
 template <int DC, Pass P, bool SCORE, class State>
 __device__ __forceinline__ bool sweep_step(State& st, int k, int n, int t0, char* cur, char* nxt, char* prv,
                                            char* pb0, char* pb1, const SweepCtx& c) {
-  if (k + 1 < n) issue_tile<DC>(c, t0 + k + 1, nxt);
+  if (!SCORE && k + 1 < n) issue_tile<DC>(c, t0 + k + 1, nxt);
   if constexpr (SCORE) {
     if (k < n) score_tile<DC, P>(st, cur, (k & 1) ? pb1 : pb0, t0 + k, k == 0, c);
   } else {
@@ -288,7 +291,7 @@ template <int DC, Pass P, bool SCORE, class State>
 __device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* k2, char* pb0, char* pb1, int t0, int t1,
                                       const SweepCtx& c) {
   const int n = t1 - t0;
-  issue_tile<DC>(c, t0, k0);
+  if (!SCORE) issue_tile<DC>(c, t0, k0);
   wait_vmcnt0();
   __syncthreads();
 #pragma unroll 1

@@ -49,7 +49,7 @@ struct Rows {
   static constexpr int BUF = kBN * ROWB;            // LDS bytes per tile
   static constexpr int ROWS = 64 / NSLOT;           // rows per load
   static constexpr int NLOAD = (kBN + ROWS - 1) / ROWS;
-  static constexpr int PER_WAVE = (NLOAD + kWaves - 1) / kWaves;
+  static constexpr int PER_WAVE = (NLOAD + kGroups - 1) / kGroups;   // value wavefronts issue the loads
   static_assert(ROWS >= 1 && (NSLOT & 1), "a row fits one load, odd slot stride");
 };
 
@@ -88,8 +88,9 @@ struct Ctx {
   int s_off, v_off;      // LDS operand offsets inside a tile
 };
 
-// Enqueue this wavefront's share of the direct-to-LDS loads of tile t of one
-// tensor: load ld copies rows [ld*ROWS, ld*ROWS + ROWS).  Keys past n_k
+// Enqueue this value wavefront's share of the direct-to-LDS loads of tile t
+// of one tensor (the score wavefronts, each step's critical path, issue
+// none): load ld copies rows [ld*ROWS, ld*ROWS + ROWS).  Keys past n_k
 // re-read key n_k - 1 (their scores are masked).  Offsets are 32-bit: one
 // (batch, head)'s keys span less than 4 GiB.
 template <int D>
@@ -98,7 +99,7 @@ __device__ inline void issue_rows(const Ctx& c, const char* base, uint32_t row_b
   using R = Rows<D>;
 #pragma unroll
   for (int i = 0; i < R::PER_WAVE; ++i) {
-    const int ld = c.wave + kWaves * i;
+    const int ld = c.group + kGroups * i;
     if (ld < R::NLOAD) {
       const int row0 = ld * R::ROWS;
       const uint32_t key = (uint32_t)min(t * kBN + row0 + lc.row, c.n_k - 1);
@@ -228,8 +229,8 @@ __device__ __forceinline__ void value_tile(ValueState& st, const char* vbuf, con
 template <int DQK, Pass P, bool SCORE, class State>
 __device__ __forceinline__ bool sweep_step(State& st, int k, int n, int t0, char* kcur, char* knxt, char* vload,
                                            char* vprev, char* pcur, char* pprev, const Ctx& c) {
-  if (k + 1 < n) issue_rows<DQK>(c, c.kbase, c.krow, c.kc, t0 + k + 1, knxt);
-  if (P != Pass::kMax && k < n) issue_rows<kDV>(c, c.vbase, c.vrow, c.vc, t0 + k, vload);
+  if (!SCORE && k + 1 < n) issue_rows<DQK>(c, c.kbase, c.krow, c.kc, t0 + k + 1, knxt);
+  if (!SCORE && P != Pass::kMax && k < n) issue_rows<kDV>(c, c.vbase, c.vrow, c.vc, t0 + k, vload);
   if constexpr (SCORE) {
     if (k < n) score_tile<DQK, P>(st, kcur, pcur, t0 + k, k == 0, c);
   } else {
@@ -244,7 +245,7 @@ template <int DQK, Pass P, bool SCORE, class State>
 __device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* v0, char* v1, char* pb0, char* pb1,
                                       int t0, int t1, const Ctx& c) {
   const int n = t1 - t0;
-  issue_rows<DQK>(c, c.kbase, c.krow, c.kc, t0, k0);
+  if (!SCORE) issue_rows<DQK>(c, c.kbase, c.krow, c.kc, t0, k0);
   wait_vmcnt0();
   __syncthreads();
 #pragma unroll 1
