@@ -423,14 +423,14 @@ __device__ __forceinline__ void value_role(SweepCtx& c, SegmentIter it, const u1
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int rl = c.group * kGroupRows + qb * 32 + (c.lane & 31);
-      float* Ld = part_L + (slot * kRowsPerBlock + rl) * DC;
 #pragma unroll
       for (int cb = 0; cb < L::CB; ++cb)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
           const int c0 = cb * 32 + gg * 8 + c.half * 4;
-          *reinterpret_cast<f32x4*>(Ld + c0) = f32x4{st.oacc[qb][cb][4 * gg], st.oacc[qb][cb][4 * gg + 1],
-                                                     st.oacc[qb][cb][4 * gg + 2], st.oacc[qb][cb][4 * gg + 3]};
+          *reinterpret_cast<f32x4*>(part_L + part_L_index(slot, rl, c0, DC)) =
+              f32x4{st.oacc[qb][cb][4 * gg], st.oacc[qb][cb][4 * gg + 1], st.oacc[qb][cb][4 * gg + 2],
+                    st.oacc[qb][cb][4 * gg + 3]};
         }
     }
   }

@@ -382,14 +382,14 @@ void attend_wide_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstrid
     for (int qb = 0; qb < QB; ++qb) {
       const float l_tot = st.l_run[qb] + __shfl_xor(st.l_run[qb], 32);
       const int rl = wave * 32 * QB + qb * 32 + (lane & 31);
-      float* Ld = part_L + (slot * kRowsPerBlock + rl) * DC;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
           const int c0 = cb * 32 + gg * 8 + half * 4;
-          *reinterpret_cast<f32x4*>(Ld + c0) = f32x4{st.oacc[qb][cb][4 * gg], st.oacc[qb][cb][4 * gg + 1],
-                                                     st.oacc[qb][cb][4 * gg + 2], st.oacc[qb][cb][4 * gg + 3]};
+          *reinterpret_cast<f32x4*>(part_L + part_L_index(slot, rl, c0, DC)) =
+              f32x4{st.oacc[qb][cb][4 * gg], st.oacc[qb][cb][4 * gg + 1], st.oacc[qb][cb][4 * gg + 2],
+                    st.oacc[qb][cb][4 * gg + 3]};
         }
       if (half == 0) {
         part_ml[(slot * kRowsPerBlock + rl) * 2 + 0] = st.m_ref[qb];

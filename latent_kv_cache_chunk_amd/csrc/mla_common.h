@@ -70,6 +70,12 @@ struct Visibility {
 // touch, in slot w + rb: a workgroup's row blocks are consecutive, so these
 // slots are distinct, and fewer than G + nrb.  The merge step finds the
 // owners of a row block's first and last unit arithmetically.
+//
+// A slot holds, for its 256 rows, (m, l) pairs and the unnormalised fp32 L
+// rows.  The bf16 kernels store L channel-quad-major inside each 32-row
+// group: float index part_L_index(slot, row, c) below, so that one 16-byte
+// store or load of a wavefront (32 rows, one channel quad per lane half)
+// covers two contiguous 512-byte runs.  The fp32 kernels keep plain rows.
 // ---------------------------------------------------------------------------
 struct Plan {
   int32_t B, H, n_q, n_k, d_c, width;   // width = d_c + d_r
@@ -116,6 +122,11 @@ __host__ __device__ inline int64_t rb_of_unit(const int64_t* units, int64_t T, i
 }
 // Slot of workgroup w's partial state for row block rb.
 __host__ __device__ inline int64_t seg_slot(int64_t w, int64_t rb) { return w + rb; }
+// Float index of channel c of row `row` (0..255) of a slot's L (bf16 kernels):
+// [row / 32][c / 4][row % 32][c % 4] inside the slot.
+__host__ __device__ inline int64_t part_L_index(int64_t slot, int row, int c, int d_c) {
+  return (slot * kRowsPerBlock + (row & ~31)) * d_c + (c >> 2) * 128 + (row & 31) * 4 + (c & 3);
+}
 
 inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 

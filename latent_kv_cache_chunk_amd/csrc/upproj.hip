@@ -11,8 +11,10 @@
 
 namespace mla {
 
+// Two wavefronts per SIMD for d_c <= 192 (the merge is latency-bound); d_c =
+// 256 needs the full register file for its 128 merged channels per lane.
 template <int DC, bool OUT_F32>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(256, DC <= 192 ? 2 : 1)
 void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restrict__ part_ml,
                         const int64_t* __restrict__ units_ws, const PartitionHeader* __restrict__ hdr,
                         int T, int rb_per_b, int n_q, int H, const u16* __restrict__ w_uv,
@@ -22,7 +24,23 @@ void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restric
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
   const int i = blockIdx.y * 128 + wave * 32 + (lane & 31);
   const bool ok = i < n_q;
-  if (blockIdx.y * 128 + wave * 32 >= n_q) return;   // no real row in this wavefront (no barriers follow)
+  const bool active = blockIdx.y * 128 + wave * 32 < n_q;   // some real row in this wavefront
+
+  // W_UV[h] (DH rows of DC bf16) staged once per workgroup; rows padded to an
+  // odd number of 16-byte slots so that the b128 operand reads are
+  // conflict-free.
+  constexpr int WROW = DC * 2 + 16;
+  __shared__ __attribute__((aligned(16))) char wsh[DH * WROW];
+  {
+    const u16* wsrc = w_uv + (int64_t)h * DH * DC;
+    constexpr int CH = DC / 8;   // 16-byte pieces per row
+    for (int q = threadIdx.x; q < DH * CH; q += 256) {
+      const int row = q / CH, ch = q - row * CH;
+      *reinterpret_cast<uint4*>(wsh + row * WROW + ch * 16) =
+          *reinterpret_cast<const uint4*>(wsrc + (int64_t)row * DC + ch * 8);
+    }
+  }
+
   const int r = h * n_q + (ok ? i : 0);
   const int64_t rb = (int64_t)b * rb_per_b + r / kRowsPerBlock;
   const int rl = r % kRowsPerBlock;
@@ -34,61 +52,61 @@ void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restric
   const int64_t* units = ph.per_block_units ? units_ws : nullptr;
   const int64_t u_first = rb_first_unit(units, T, rb), u_last = rb_first_unit(units, T, rb + 1) - 1;
   const int64_t wa = unit_owner(u_first, U, G), wb = unit_owner(u_last, U, G);
-  float M = -INFINITY;
-  for (int64_t w = wa; w <= wb; ++w) {
-    const int64_t sl = seg_slot(w, rb);
-    M = fmaxf(M, part_ml[(sl * kRowsPerBlock + rl) * 2]);
-  }
-  float lsum = 0.f;
-  for (int64_t w = wa; w <= wb; ++w) {
-    const int64_t sl = seg_slot(w, rb);
-    const float* ml = part_ml + (sl * kRowsPerBlock + rl) * 2;
-    lsum += exp2f(ml[0] - M) * ml[1];
-  }
-  const float inv_l = 1.f / lsum;
 
-  // L of this lane's row and columns {ks*16 + half*8 + e}: one pass over the
-  // segments, each segment's weight computed once and all of its columns
-  // loaded together (rows of short chunks can have over a hundred segments).
+  // L of this lane's row and columns {ks*16 + half*8 + e}, merged over the
+  // segments in one pass with a running max M: what is summed so far is
+  // rescaled by 2^(M_old - M_new) when a segment raises it.  A segment with
+  // no visible key of the row has m = -inf and weight 0.  One segment's
+  // loads at a time keep the wavefront at two per SIMD (rows of short chunks
+  // can have over a hundred segments).
+  float M = -INFINITY, lsum = 0.f;
   float lc[KSTEPS][8];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) lc[ks][e] = 0.f;
-#pragma unroll 2
-  for (int64_t w = wa; w <= wb; ++w) {
+#pragma unroll 1
+  for (int64_t w = active ? wa : wb + 1; w <= wb; ++w) {
     const int64_t sl = seg_slot(w, rb);
-    const float wgt = exp2f(part_ml[(sl * kRowsPerBlock + rl) * 2] - M) * inv_l;
-    const float* src = part_L + (sl * kRowsPerBlock + rl) * DC + half * 8;
+    const float m_w = part_ml[(sl * kRowsPerBlock + rl) * 2], l_w = part_ml[(sl * kRowsPerBlock + rl) * 2 + 1];
+    const float m_new = fmaxf(M, m_w);
+    const float keep = M == -INFINITY ? 0.f : exp2f(M - m_new);
+    const float wgt = m_w == -INFINITY ? 0.f : exp2f(m_w - m_new);
+    M = m_new;
+    lsum = fmaf(lsum, keep, wgt * l_w);
+    const float* src = part_L + part_L_index(sl, rl, half * 8, DC);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + ks * 16);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + ks * 16 + 4);
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + ks * 512);         // channels ks*16 + half*8 + 0..3
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + ks * 512 + 128);   // channels ks*16 + half*8 + 4..7
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        lc[ks][e] = fmaf(wgt, x0[e], lc[ks][e]);
-        lc[ks][4 + e] = fmaf(wgt, x1[e], lc[ks][4 + e]);
+        lc[ks][e] = fmaf(wgt, x0[e], lc[ks][e] * keep);
+        lc[ks][4 + e] = fmaf(wgt, x1[e], lc[ks][4 + e] * keep);
       }
     }
   }
+  const float inv_l = 1.f / lsum;
+  __syncthreads();         // W_UV staged
+  if (!active) return;     // no barriers follow
 
   f32x16 acc[DH / 32];
 #pragma unroll
   for (int db = 0; db < DH / 32; ++db) acc[db] = f32x16{};
-  const u16* wv = w_uv + (int64_t)h * DH * DC;
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
     const int c0 = ks * 16 + half * 8;
     bf16x8 hi, lo;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const bf16x2 h2 = to_bf16x2(ok ? lc[ks][e] : 0.f, ok ? lc[ks][e + 1] : 0.f);
-      const bf16x2 l2 = to_bf16x2(ok ? lc[ks][e] - (float)h2[0] : 0.f, ok ? lc[ks][e + 1] - (float)h2[1] : 0.f);
+      const float v0 = ok ? lc[ks][e] * inv_l : 0.f, v1 = ok ? lc[ks][e + 1] * inv_l : 0.f;
+      const bf16x2 h2 = to_bf16x2(v0, v1);
+      const bf16x2 l2 = to_bf16x2(v0 - (float)h2[0], v1 - (float)h2[1]);
       hi[e] = h2[0]; hi[e + 1] = h2[1]; lo[e] = l2[0]; lo[e + 1] = l2[1];
     }
 #pragma unroll
     for (int db = 0; db < DH / 32; ++db) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(wv + (int64_t)(db * 32 + (lane & 31)) * DC + c0);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(wsh + (db * 32 + (lane & 31)) * WROW + c0 * 2);
       acc[db] = mfma_32x32x16(a, hi, acc[db]);
       acc[db] = mfma_32x32x16(a, lo, acc[db]);
     }
