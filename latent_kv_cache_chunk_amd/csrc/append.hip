@@ -12,17 +12,34 @@ namespace mla {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// One workgroup computes 32 tokens x one block of 32 outputs with
-// bf16 MFMA 32x32x16 and fp32 accumulation; a launch has (tokens / 32) x
-// ((d_c + d_r) / 32) workgroups, enough to fill the chip at one chunk.  The
-// four wavefronts split the reduction over d_model (a quarter each, loads
-// issued eight k-steps ahead) and their fp32 partial sums are added in LDS, in
-// a fixed order.  The product is formed transposed, C^T[n][token] = sum_k
-// W[n][k] x[token][k]: weight rows (n) are the A operand, read from global
-// memory (the whole [W_DKV; W_KR] is 688 KB at D = 1536, d_c = 192, and stays
-// in L2), hidden states are the B operand.  In the epilogue each thread owns
-// four consecutive outputs of one token, so the RoPE pairs are thread-local
-// and the store is 8 bytes.
+// One workgroup computes 32 tokens x one block of 32 outputs with bf16 MFMA
+// 32x32x16 and fp32 accumulation; a launch has (tokens / 32) x ((d_c + d_r) /
+// 32) workgroups, enough to fill the chip at one chunk.  The product is formed
+// transposed, C^T[n][token] = sum_k W[n][k] x[token][k]: weight rows (n) are
+// the A operand (the whole [W_DKV; W_KR] is 688 KB at D = 1536, d_c = 192, and
+// stays in L2), hidden states the B operand.
+//
+// d_model is cut into 64-wide chunks dealt round robin to the four
+// wavefronts; their fp32 partial sums are added in LDS in a fixed order.  A
+// chunk is 32 rows x 128 bytes of x and of W.  Global loads are row-major
+// (eight lanes read one row's 128 bytes, so a load instruction covers eight
+// whole cache lines), two chunks in flight in registers; each chunk then
+// goes through the wavefront's own 8 KB of LDS, where 16-byte piece p of row r
+// sits in slot p ^ (r & 7), and comes back in MFMA operand layout.  Both the
+// row-major writes and the operand reads (eight rows per 128 bytes of banks)
+// are conflict-free.  Which eight k of a 16-wide k-step a lane half holds does
+// not change the sum: lane half h of k-step j holds piece 2j + h of the chunk,
+// in A and B alike.
+//
+// In the epilogue each thread owns four consecutive outputs of one token, so
+// the RoPE pairs are thread-local and the store is 8 bytes.
+constexpr int kAppendChunk = 64;          // k per chunk
+constexpr int kAppendRing = 2;            // chunks in flight per wavefront
+
+struct AppendChunk {
+  u32x4 x[4], w[4];                       // rows q*8 + lane/8, piece lane%8
+};
+
 template <int NB>
 __global__ __launch_bounds__(256)
 void append_bf16_kernel(const u16* __restrict__ x, int D, int ntok, int n_new,
@@ -30,7 +47,7 @@ void append_bf16_kernel(const u16* __restrict__ x, int D, int ntok, int n_new,
                         const int* __restrict__ pos, u16* __restrict__ cache, int cap, int off,
                         RopeSpec rope) {
   constexpr int W = NB * 32;
-  constexpr int UNROLL = 8;
+  __shared__ __attribute__((aligned(16))) char stage[4][2][32 * 128];   // [wave][x | w] chunk rows
   __shared__ float part[4][32][32 + 4];     // per-wave partial sums [token][n - n_base]
 
   // Workgroup id -> (token block tb, output block nb) so that the output
@@ -44,31 +61,77 @@ void append_bf16_kernel(const u16* __restrict__ x, int D, int ntok, int n_new,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tok0 = tb * 32;
   const int n_base = nb * 32;
-  const int my_tok = tok0 + (lane & 31);
-  const bool tok_ok = my_tok < ntok;
-  const int kq = D / 4;                                  // this wave's share of the reduction
-  const int kbeg = wave * kq;
-  const u16* xrow = x + (int64_t)(tok_ok ? my_tok : 0) * D + kbeg + half * 8;
-  const int n = n_base + (lane & 31);
-  const u16* wrow = (n < d_c ? w_dkv + (int64_t)n * D : w_kr + (int64_t)(n - d_c) * D) + kbeg + half * 8;
 
-  f32x16 acc = {};
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  const int ksteps = kq / 16;
-  int k = 0;
-  for (; k + UNROLL <= ksteps; k += UNROLL) {
-    bf16x8 bx[UNROLL], aw[UNROLL];
+  // global row pointers of this lane's four x rows and four W rows (row-major loads)
+  const int lrow = lane >> 3, piece = lane & 7;
+  const u16* xr[4];
+  const u16* wr[4];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      bx[u] = tok_ok ? *reinterpret_cast<const bf16x8*>(xrow + (k + u) * 16) : __builtin_bit_cast(bf16x8, zero);
-      aw[u] = *reinterpret_cast<const bf16x8*>(wrow + (k + u) * 16);
+  for (int q = 0; q < 4; ++q) {
+    const int tok = min(tok0 + q * 8 + lrow, ntok - 1);   // rows past the last token re-read it
+    xr[q] = x + (int64_t)tok * D + piece * 8;
+    const int n = n_base + q * 8 + lrow;
+    wr[q] = (n < d_c ? w_dkv + (int64_t)n * D : w_kr + (int64_t)(n - d_c) * D) + piece * 8;
+  }
+  char* xs = stage[wave][0];
+  char* ws = stage[wave][1];
+  const int wslot = lrow * 128 + ((piece ^ lrow) * 16);            // row-major write slot (row & 7 == lrow)
+  const int r = lane & 31;
+  const int nchunks = D / kAppendChunk;
+  const int mine = (nchunks - wave + 3) / 4;                       // chunks wave, wave + 4, ...
+
+  // Chunk i of this wavefront (clamped to its last one: the prologue of a
+  // wavefront with a single chunk loads it twice and uses it once).
+  auto issue = [&](AppendChunk& ck, int i) {
+    const int k0 = (wave + 4 * min(i, mine - 1)) * kAppendChunk;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ck.x[q] = *reinterpret_cast<const u32x4*>(xr[q] + k0);
+      ck.w[q] = *reinterpret_cast<const u32x4*>(wr[q] + k0);
+    }
+  };
+  f32x16 acc = {};
+  auto consume = [&](const AppendChunk& ck) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<u32x4*>(xs + q * 1024 + wslot) = ck.x[q];
+      *reinterpret_cast<u32x4*>(ws + q * 1024 + wslot) = ck.w[q];
+    }
+    // the wavefront's LDS accesses run in order; these only keep the
+    // compiler from moving the operand reads above other lanes' writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    bf16x8 a[kAppendChunk / 16], b[kAppendChunk / 16];
+#pragma unroll
+    for (int j = 0; j < kAppendChunk / 16; ++j) {
+      const int off_b = r * 128 + (((2 * j + half) ^ (r & 7)) * 16);
+      a[j] = *reinterpret_cast<const bf16x8*>(ws + off_b);
+      b[j] = *reinterpret_cast<const bf16x8*>(xs + off_b);
     }
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) acc = mfma_32x32x16(aw[u], bx[u], acc);
-  }
-  for (; k < ksteps; ++k) {
-    const bf16x8 bx = tok_ok ? *reinterpret_cast<const bf16x8*>(xrow + k * 16) : __builtin_bit_cast(bf16x8, zero);
-    acc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(wrow + k * 16), bx, acc);
+    for (int j = 0; j < kAppendChunk / 16; ++j) acc = mfma_32x32x16(a[j], b[j], acc);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // Two chunks in flight.  Every pass of the loop issues exactly two more (so
+  // the wait before each chunk's first use is the same on every path); the
+  // last two are consumed after it.
+  if (mine > 0) {
+    AppendChunk c0, c1;
+    issue(c0, 0);
+    issue(c1, 1);
+    int i = 0;
+#pragma unroll 1
+    for (; i + kAppendRing < mine; i += kAppendRing) {
+      consume(c0);
+      issue(c0, i + 2);
+      consume(c1);
+      issue(c1, i + 3);
+    }
+    consume(c0);
+    if (i + 1 < mine) consume(c1);
   }
   // partial sums -> LDS: lane holds token (lane & 31), outputs n_base + 8g + 4*half + t
 #pragma unroll

@@ -60,6 +60,25 @@ def test_append_exact_tier_bytes(d_c):
     assert np.array_equal(gb, want), f"{np.count_nonzero(gb != want)} of {gb.size} bf16 values differ"
 
 
+@pytest.mark.parametrize("d_model", [64, 320, 576, 2048])
+def test_append_exact_tier_other_widths(d_model):
+    """d_model is dealt to the four wavefronts in 64-wide chunks round robin:
+    64 leaves three of them without a chunk, 320 and 576 give them unequal
+    counts (one of them a single chunk), 2048 runs the steady-state loop."""
+    mla = need_gpu()
+    from dataclasses import replace
+    wl = replace(synth.TINY, d_model=d_model, batch=2)
+    inp = synth.append_inputs_exact(wl, seed=3)
+    cap, off = wl.n_q + 5, 3
+    got = _run_append(mla, wl, inp, cap, off)
+    ref = oracle.cache_append(np.zeros((wl.batch, cap, wl.d_c + wl.d_r)), np64(inp["x"]), np64(inp["w_dkv"]),
+                              np64(inp["w_kr"]), inp["pos"].numpy(), off, split=wl.rope_split, theta=wl.theta)
+    want = np.full((wl.batch, cap, wl.d_c + wl.d_r), 0x7F7F, np.uint16)
+    want[:, off:off + wl.n_q] = oracle.bf16_bits(ref[:, off:off + wl.n_q])
+    gb = _bits(got)
+    assert np.array_equal(gb, want), f"{np.count_nonzero(gb != want)} of {gb.size} bf16 values differ"
+
+
 def _error_bound(x, w_all, pos, wl):
     """Rigorous bound on |fp32 GPU value - exact value| per output element."""
     D = x.shape[-1]
