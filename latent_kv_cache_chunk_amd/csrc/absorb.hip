@@ -30,10 +30,14 @@ void rope_table_kernel(const int* __restrict__ q_pos, int n_q, int pairs, RopeSp
 // Content part on MFMA: C^T[c][i] = sum_d W_UK[h][d][c] q[i][d].  W_UK[h]
 // (128 x d_c) is staged once in LDS, rows padded to an odd number of 16-byte
 // slots, and its transpose is read as the A operand with ds_read_tr16_b64
-// (two reads give a lane eight d of one column c).  Those eight d are
-// {4h..4h+3, 8+4h..8+4h+3} of the 16-wide k-step for lane half h, so the B
-// operand takes q in the same order (two 8-byte loads).  The rotated
-// positional part comes from the (cos, sin) table.
+// (two reads give a lane eight d of one column c).  Those reads hand lane
+// half h the LDS rows {4h..4h+3, 8+4h..8+4h+3} of each 16-row k-step, so
+// W_UK row d is staged in LDS row d with bits 2 and 3 swapped: lane half h
+// then holds d = 8h .. 8h+7 in order, and q is loaded as one 16-byte piece
+// per k-step.  The rotated positional part comes from the (cos, sin) table.
+// Finished rows go through LDS (over the W_UK stage, after a barrier): a
+// wavefront's 32 rows of q~ are contiguous in memory and leave as whole
+// 16-byte pieces of consecutive addresses.
 template <int DC>
 __global__ __launch_bounds__(256)
 void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
@@ -43,70 +47,94 @@ void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
   constexpr int DH = 128, DR = 32, W = DC + DR, CB = DC / 32;
   constexpr int NCH = DC / 8, ROWB = (NCH + 1) * 16;
   static_assert((NCH + 1) & 1, "odd slot stride");
-  __shared__ __attribute__((aligned(16))) char wl[DH * ROWB];
+  constexpr int OROW = W * 2 + 16;                       // staged output row (odd number of 16-byte slots)
+  static_assert(((W * 2 + 16) / 16) & 1, "odd slot stride");
+  constexpr int WBYTES = DH * ROWB, OBYTES = 4 * 32 * OROW;
+  __shared__ __attribute__((aligned(16))) char wl[WBYTES > OBYTES ? WBYTES : OBYTES];
   const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
-  const int i = blockIdx.y * 128 + wave * 32 + (lane & 31);
+  const int i0 = blockIdx.y * 128 + wave * 32;           // first query of this wavefront
+  const int i = i0 + (lane & 31);
   const bool ok = i < n_q;
 
   const u16* wk = w_uk + (int64_t)h * DH * DC;
   for (int idx = threadIdx.x; idx < DH * NCH; idx += 256) {
     const int r = idx / NCH, ch = idx - r * NCH;
-    *reinterpret_cast<uint4*>(wl + r * ROWB + ch * 16) = *reinterpret_cast<const uint4*>(wk + r * DC + ch * 8);
+    const int rs = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+    *reinterpret_cast<uint4*>(wl + rs * ROWB + ch * 16) = *reinterpret_cast<const uint4*>(wk + r * DC + ch * 8);
   }
 
   const int64_t qrow_off = (((int64_t)b * n_q + (ok ? i : 0)) * H + h);
-  const u16* qrow = q + qrow_off * DH + half * 4;
+  const u16* qrow = q + qrow_off * DH + half * 8;
   bf16x8 qf[DH / 16];
 #pragma unroll
-  for (int ks = 0; ks < DH / 16; ++ks) {
-    const uint2 lo = ok ? *reinterpret_cast<const uint2*>(qrow + ks * 16) : make_uint2(0, 0);
-    const uint2 hi = ok ? *reinterpret_cast<const uint2*>(qrow + ks * 16 + 8) : make_uint2(0, 0);
-    qf[ks] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-  }
+  for (int ks = 0; ks < DH / 16; ++ks)
+    qf[ks] = ok ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16) : bf16x8{};
   __syncthreads();
 
   const int g = lane >> 4, j = lane & 15;
   const char* abase = wl + ((g >> 1) * 4 + (j >> 2)) * ROWB + (16 * (g & 1) + 4 * (j & 3)) * 2;
-  u16* orow = qt + ((int64_t)b * rows_pad_b + (int64_t)h * n_q + i) * W;
-#pragma unroll 1
+  f32x16 acc[CB];
+#pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    f32x16 acc = {};
+    acc[cb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks) {
       const char* ab = abase + ks * 16 * ROWB + cb * 64;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)ab);
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ab + 8 * ROWB));
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc = mfma_32x32x16(a, qf[ks], acc);
-    }
-    if (ok) {
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int c0 = cb * 32 + gg * 8 + half * 4;
-        const uint32_t lo = bf16x2_bits(to_bf16x2(acc[4 * gg] * qscale, acc[4 * gg + 1] * qscale));
-        const uint32_t hi = bf16x2_bits(to_bf16x2(acc[4 * gg + 2] * qscale, acc[4 * gg + 3] * qscale));
-        *reinterpret_cast<uint2*>(orow + c0) = make_uint2(lo, hi);
-      }
+      acc[cb] = mfma_32x32x16(a, qf[ks], acc[cb]);
     }
   }
+  __syncthreads();   // every wavefront is done with the W_UK stage
 
+  // this wavefront's 32 output rows, staged in LDS
+  char* orow = wl + wave * 32 * OROW + (lane & 31) * OROW;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const int c0 = cb * 32 + gg * 8 + half * 4;
+      const uint32_t lo = bf16x2_bits(to_bf16x2(acc[cb][4 * gg] * qscale, acc[cb][4 * gg + 1] * qscale));
+      const uint32_t hi = bf16x2_bits(to_bf16x2(acc[cb][4 * gg + 2] * qscale, acc[cb][4 * gg + 3] * qscale));
+      *reinterpret_cast<uint2*>(orow + c0 * 2) = make_uint2(lo, hi);
+    }
   // Positional part: lane half `half` rotates pairs 8*half .. 8*half+7.
   if (ok) {
     const u16* qr = q_r + qrow_off * DR + half * 16;
     const f32x2* cs = rope_cs + (int64_t)i * (DR / 2) + half * 8;
+    const uint4 r0 = *reinterpret_cast<const uint4*>(qr), r1 = *reinterpret_cast<const uint4*>(qr + 8);
+    const uint32_t in[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
     uint32_t outw[8];
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
-      const float x0 = (float)__builtin_bit_cast(__bf16, qr[2 * pp]);
-      const float x1 = (float)__builtin_bit_cast(__bf16, qr[2 * pp + 1]);
+      const float x0 = __builtin_bit_cast(float, in[pp] << 16);
+      const float x1 = __builtin_bit_cast(float, in[pp] & 0xFFFF0000u);
       const f32x2 r = cs[pp];
       const float y0 = fmaf(x0, r[0], -(x1 * r[1])), y1 = fmaf(x0, r[1], x1 * r[0]);
       outw[pp] = bf16x2_bits(to_bf16x2(y0 * qscale, y1 * qscale));
     }
-    uint4* o = reinterpret_cast<uint4*>(orow + DC + half * 16);
+    uint4* o = reinterpret_cast<uint4*>(orow + (DC + half * 16) * 2);
     o[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
     o[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
+  }
+  // the wavefront's LDS accesses run in order; these keep the compiler from
+  // moving the copy-out reads above other lanes' writes
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // copy-out: rows h*n_q + i0 .. of this sample are consecutive in q~
+  const int nrows = min(32, n_q - i0);
+  if (nrows > 0) {
+    constexpr int PIECES = W * 2 / 16;                   // 16-byte pieces per row
+    char* dst = reinterpret_cast<char*>(qt + ((int64_t)b * rows_pad_b + (int64_t)h * n_q + i0) * W);
+    const char* src = wl + wave * 32 * OROW;
+    for (int pc = lane; pc < nrows * PIECES; pc += 64) {
+      const int row = pc / PIECES, col = pc - row * PIECES;
+      *reinterpret_cast<uint4*>(dst + (int64_t)pc * 16) = *reinterpret_cast<const uint4*>(src + row * OROW + col * 16);
+    }
   }
 
   // Padding rows after the last real row of each sample are zero so that the
