@@ -236,10 +236,10 @@ int32_t check_mha_workspace(const mla::MhaPlan& p, const void* ws, int64_t bytes
   return MLA_OK;
 }
 
-int32_t do_mha_attend(const mla::MhaPlan& p, const void* k, const void* v, int64_t cap, float scale, int32_t out_dtype,
-                      void* out, void* ws, hipStream_t s, const char* what) {
+int32_t do_mha_attend(const mla::MhaPlan& p, const void* k, const void* v, int64_t cap, bool head_major, float scale,
+                      int32_t out_dtype, void* out, void* ws, hipStream_t s, const char* what) {
   mla::MhaAttendArgs a{};
-  a.k = k; a.v = v; a.cap = cap; a.headroom = attend_headroom();
+  a.k = k; a.v = v; a.cap = cap; a.head_major = head_major; a.headroom = attend_headroom();
   a.qscale = (float)((double)scale * mla::kLog2e);
   a.out = out; a.out_f32 = out_dtype == MLA_F32; a.workspace = ws;
   return finish(mla::launch_mha_attend(p, a, s), s, what);
@@ -275,7 +275,7 @@ int32_t mla_mha_attend(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t
   mla::MhaQueryArgs qa{};
   qa.q = q; qa.workspace = workspace;
   if ((st = finish(mla::launch_mha_prep_q(p, qa, s), s, "mla_mha_attend"))) return st;
-  return do_mha_attend(p, k, v, cache_capacity, softmax_scale, out_dtype, out, workspace, s, "mla_mha_attend");
+  return do_mha_attend(p, k, v, cache_capacity, false, softmax_scale, out_dtype, out, workspace, s, "mla_mha_attend");
 }
 
 int64_t mla_chunk_attend_expanded_workspace_bytes(const mla_dims* dims, int32_t n_q, int32_t n_k) {
@@ -314,7 +314,7 @@ int32_t mla_chunk_attend_expanded(const mla_dims* dims, int32_t out_dtype, const
   ua.cache = cache; ua.cap = cache_capacity; ua.d_c = dims->d_c; ua.w_uk = w_uk; ua.w_uv = w_uv; ua.workspace = workspace;
   if ((st = finish(mla::launch_mha_uplift(p, ua, s), s, "mla_chunk_attend_expanded"))) return st;
   const char* ws = (const char*)workspace;
-  return do_mha_attend(p, ws + p.off_k, ws + p.off_v, n_k, softmax_scale, out_dtype, out, workspace, s,
+  return do_mha_attend(p, ws + p.off_k, ws + p.off_v, n_k, true, softmax_scale, out_dtype, out, workspace, s,
                        "mla_chunk_attend_expanded");
 }
 

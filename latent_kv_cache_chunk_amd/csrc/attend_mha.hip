@@ -257,9 +257,10 @@ __device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* v0, c
 
 struct Problem {
   const u16* q;          // queries [B*H][rows_pad_h][DQK], bf16, unscaled
-  const u16* k;          // [B, cap, H, DQK]
-  const u16* v;          // [B, cap, H, kDV]
+  const u16* k;          // [B, cap, H, DQK], or [B, H, cap, DQK] when head_major
+  const u16* v;          // [B, cap, H, kDV], or [B, H, cap, kDV] when head_major
   int64_t cap;
+  bool head_major;
   int H, n_k, rows_pad_h, rb_per_bh, T;
   int64_t U;
   int G;
@@ -274,7 +275,8 @@ template <int DQK>
 __device__ __forceinline__ void begin_segment(Ctx& c, const Problem& pr, int64_t rb) {
   const int64_t bh = rb / pr.rb_per_bh;
   const int b = (int)(bh / pr.H), h = (int)(bh - (int64_t)b * pr.H);
-  const int64_t tok0 = (int64_t)b * pr.cap * pr.H + h;
+  // row (of DQK or kDV elements) of key 0 of this (batch, head)
+  const int64_t tok0 = pr.head_major ? ((int64_t)b * pr.H + h) * pr.cap : (int64_t)b * pr.cap * pr.H + h;
   c.kbase = reinterpret_cast<const char*>(pr.k + tok0 * DQK);
   c.vbase = reinterpret_cast<const char*>(pr.v + tok0 * kDV);
 }
@@ -379,8 +381,8 @@ void mha_attend_kernel(Problem pr) {
   __shared__ __attribute__((aligned(1024))) char pbuf1[L::PBUF];
   Ctx c;
   c.n_k = pr.n_k;
-  c.krow = (uint32_t)pr.H * DQK * 2;
-  c.vrow = (uint32_t)pr.H * kDV * 2;
+  c.krow = (uint32_t)(pr.head_major ? 1 : pr.H) * DQK * 2;
+  c.vrow = (uint32_t)(pr.head_major ? 1 : pr.H) * kDV * 2;
   c.lane = threadIdx.x & 63;
   c.half = c.lane >> 5;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -491,17 +493,21 @@ void mha_prep_q_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r, c
   }
 }
 
-// Per-head keys and values from the latent cache (non-absorbed form):
-//   K[b, j, h, 0:dh]   = W_UK[h] c_j,   K[b, j, h, dh:dh+dr] = k_R,j
-//   V[b, j, h, :]      = W_UV[h] c_j
+// Per-head keys and values from the latent cache (non-absorbed form), head
+// major so that the keys of one (batch, head) are contiguous:
+//   K[b, h, j, 0:dh]   = W_UK[h] c_j,   K[b, h, j, dh:dh+dr] = k_R,j
+//   V[b, h, j, :]      = W_UV[h] c_j
 // Workgroup: 256 tokens (32 per wavefront) of one head, keys (blockIdx.z =
 // 0) or values (1).  The head's 128 x d_c weight block is staged once in LDS
 // (rows padded by 16 bytes so the 32 rows one b128 read touches spread over
 // the banks); each wavefront keeps its tokens' latent rows in registers as
 // the B operand and runs the four 32-output blocks through bf16 MFMA
-// 32x32x16 with fp32 accumulation and one rounding to bf16.  Key workgroups
-// also copy k_R into their tokens' K rows.  K and V hold exactly n_k keys
-// per sample.
+// 32x32x16 with fp32 accumulation and one rounding to bf16.  Each block is
+// staged in LDS so that four lanes store a token's 64 bytes of it together;
+// the rows of consecutive tokens are adjacent.  The grid is about one round
+// of workgroups: each loads its head's weights once and loops over 256-token
+// blocks.  Key workgroups also copy k_R
+// into their tokens' K rows.  K and V hold exactly n_k keys per sample.
 template <int DC>
 __global__ __launch_bounds__(512)
 void mha_uplift_kernel(const u16* __restrict__ cache, int64_t cap, int n_k, int ntok, int H,
@@ -509,63 +515,71 @@ void mha_uplift_kernel(const u16* __restrict__ cache, int64_t cap, int n_k, int 
                        u16* __restrict__ K, u16* __restrict__ V) {
   constexpr int W = DC + 32, DH = 128, DQK = DH + 32, KS = DC / 16, WROW = DC * 2 + 16, CPR = DC / 8;
   __shared__ __attribute__((aligned(16))) char wt[DH * WROW];
-  __shared__ __attribute__((aligned(16))) char stage[8][32 * 64];   // per wavefront: 32 tokens x 32 outputs
+  constexpr int SROW = DQK * 2 + 16;   // staged output row: odd number of 16-byte slots
+  __shared__ __attribute__((aligned(16))) char stage[8][32 * SROW];   // per wavefront: its 32 output rows
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
   const int h = blockIdx.y;
   const bool is_v = blockIdx.z != 0;
+  const int drow = is_v ? DH : DQK;    // elements per output row
   const u16* wsrc = (is_v ? w_uv : w_uk) + (int64_t)h * DH * DC;
   for (int idx = threadIdx.x; idx < DH * CPR; idx += 512) {
     const int r = idx / CPR, ch = idx - r * CPR;
     *reinterpret_cast<uint4*>(wt + r * WROW + ch * 16) = *reinterpret_cast<const uint4*>(wsrc + r * DC + ch * 8);
   }
-  const int tok = blockIdx.x * 256 + wave * 32 + (lane & 31);
-  const int my_tok = min(tok, ntok - 1);
-  const int b = my_tok / n_k, j = my_tok - b * n_k;
-  const u16* crow = cache + ((int64_t)b * cap + j) * W;
-  bf16x8 cf[KS];
-#pragma unroll
-  for (int k = 0; k < KS; ++k) cf[k] = *reinterpret_cast<const bf16x8*>(crow + k * 16 + half * 8);
-  const int64_t kv_row = ((int64_t)b * n_k + j) * H + h;
-  u16* dst = is_v ? V + kv_row * DH : K + kv_row * DQK;
-  const bool live = tok < ntok;
-  // the rows this lane stores from the staging area: token (lane >> 2) + 16u, 16-byte piece (lane & 3)
+  u16* out = is_v ? V : K;
   char* st = stage[wave];
-  u16* sdst[2];
-  bool slive[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int t = tok - (lane & 31) + (lane >> 2) + 16 * u;   // token of the wavefront's 32
-    slive[u] = t < ntok;
-    const int tt = min(t, ntok - 1);
-    const int tb = tt / n_k, tj = tt - tb * n_k;
-    const int64_t row = ((int64_t)tb * n_k + tj) * H + h;
-    sdst[u] = (is_v ? V + row * DH : K + row * DQK) + (lane & 3) * 8;
-  }
+  char* srow = st + (lane & 31) * SROW;
+  const int pieces = drow / 8;         // 16-byte pieces per output row
   __syncthreads();
+  // 256-token blocks blockIdx.x, blockIdx.x + gridDim.x, ...: the weight
+  // stage is loaded once per workgroup, and the wavefronts run their blocks
+  // without further barriers (each uses only its own staging area).
 #pragma unroll 1
-  for (int ob = 0; ob < 4; ++ob) {
-    const char* a = wt + (ob * 32 + (lane & 31)) * WROW + half * 16;
-    f32x16 acc = {};
+  for (int tb = blockIdx.x; tb * 256 < ntok; tb += gridDim.x) {
+    const int tok0 = tb * 256 + wave * 32;   // first token (b * n_k + j) of this wavefront
+    const int tok = tok0 + (lane & 31);
+    const int my_tok = min(tok, ntok - 1);
+    const int b = my_tok / n_k, j = my_tok - b * n_k;
+    const u16* crow = cache + ((int64_t)b * cap + j) * W;
+    bf16x8 cf[KS];
 #pragma unroll
-    for (int k = 0; k < KS; ++k) acc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(a + k * 32), cf[k], acc);
-    // lane holds its token's outputs 32*ob + 8g + 4*half + t, t = 0..3: stage them, then store
-    // each token's 64 bytes of this block as four 16-byte pieces from four lanes
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      *reinterpret_cast<uint2*>(st + (lane & 31) * 64 + (g * 8 + half * 4) * 2) =
-          make_uint2(bf16x2_bits(to_bf16x2(acc[4 * g], acc[4 * g + 1])),
-                     bf16x2_bits(to_bf16x2(acc[4 * g + 2], acc[4 * g + 3])));
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint4 piece = *reinterpret_cast<const uint4*>(st + ((lane >> 2) + 16 * u) * 64 + (lane & 3) * 16);
-      if (slive[u]) *reinterpret_cast<uint4*>(sdst[u] + ob * 32) = piece;
+    for (int k = 0; k < KS; ++k) cf[k] = *reinterpret_cast<const bf16x8*>(crow + k * 16 + half * 8);
+    if (!is_v) {   // the positional key, shared by every head
+      const uint4* kr = reinterpret_cast<const uint4*>(crow + DC + half * 16);
+      uint4* kd = reinterpret_cast<uint4*>(srow + (DH + half * 16) * 2);
+      kd[0] = kr[0];
+      kd[1] = kr[1];
     }
-  }
-  if (!is_v && live) {   // the positional key, shared by every head
-    const uint4* kr = reinterpret_cast<const uint4*>(crow + DC + half * 16);
-    uint4* kd = reinterpret_cast<uint4*>(dst + DH + half * 16);
-    kd[0] = kr[0];
-    kd[1] = kr[1];
+#pragma unroll 1
+    for (int ob = 0; ob < 4; ++ob) {
+      const char* a = wt + (ob * 32 + (lane & 31)) * WROW + half * 16;
+      f32x16 acc = {};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) acc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(a + k * 32), cf[k], acc);
+      // lane holds its token's outputs 32*ob + 8g + 4*half + t, t = 0..3
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<uint2*>(srow + (ob * 32 + g * 8 + half * 4) * 2) =
+            make_uint2(bf16x2_bits(to_bf16x2(acc[4 * g], acc[4 * g + 1])),
+                       bf16x2_bits(to_bf16x2(acc[4 * g + 2], acc[4 * g + 3])));
+    }
+    // the wavefront's LDS accesses run in order; these keep the compiler
+    // from moving the copy-out reads above other lanes' writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int pc = lane; pc < 32 * pieces; pc += 64) {
+      const int tw = pc / pieces, col = pc - tw * pieces;
+      const int t = tok0 + tw;
+      if (t < ntok) {
+        const int ub = t / n_k, uj = t - ub * n_k;
+        *reinterpret_cast<uint4*>(out + (((int64_t)ub * H + h) * n_k + uj) * drow + col * 8) =
+            *reinterpret_cast<const uint4*>(st + tw * SROW + col * 16);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -612,7 +626,11 @@ hipError_t launch_mha_prep_q(const MhaPlan& p, const MhaQueryArgs& a, hipStream_
 hipError_t launch_mha_uplift(const MhaPlan& p, const MhaUpliftArgs& a, hipStream_t s) {
   char* ws = (char*)a.workspace;
   const int ntok = p.B * p.n_k;
-  const dim3 grid((ntok + 255) / 256, p.H, 2), block(512);
+  // about one round of workgroups (two per compute unit), each looping over
+  // 256-token blocks
+  const int blocks = (ntok + 255) / 256;
+  const int per_head = std::max(1, std::min(blocks, kPartitionCUs / (2 * p.H)));
+  const dim3 grid((unsigned)per_head, p.H, 2), block(512);
   u16* K = (u16*)(ws + p.off_k);
   u16* V = (u16*)(ws + p.off_v);
   const u16* c = (const u16*)a.cache;
@@ -635,6 +653,7 @@ hipError_t launch_mha_attend(const MhaPlan& p, const MhaAttendArgs& a, hipStream
   pr.k = (const u16*)a.k;
   pr.v = (const u16*)a.v;
   pr.cap = a.cap;
+  pr.head_major = a.head_major;
   pr.H = p.H; pr.n_k = p.n_k; pr.rows_pad_h = p.rows_pad_h; pr.rb_per_bh = p.rb_per_bh; pr.T = p.T;
   pr.U = p.U; pr.G = p.G; pr.headroom = a.headroom; pr.qscale = a.qscale;
   pr.part_L = (float*)(ws + p.off_L);

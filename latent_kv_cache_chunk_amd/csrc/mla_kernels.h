@@ -55,7 +55,7 @@ struct MhaPlan {
   int64_t U;                       // units nrb * T
   int32_t G;                       // attention workgroups
   // byte offsets inside the workspace: scaled queries, partial states,
-  // and (non-absorbed form) the materialised per-head K and V
+  // and (non-absorbed form) the materialised per-head K [B, H, n_k, dqk] and V [B, H, n_k, 128]
   int64_t off_qt, off_L, off_ml, off_k, off_v, total;
 };
 
@@ -79,9 +79,10 @@ struct MhaUpliftArgs {
 };
 
 struct MhaAttendArgs {
-  const void* k;        // [B, cap, H, dqk]
-  const void* v;        // [B, cap, H, 128]
+  const void* k;        // [B, cap, H, dqk], or [B, H, cap, dqk] when head_major
+  const void* v;        // [B, cap, H, 128], or [B, H, cap, 128] when head_major
   int64_t cap;
+  bool head_major;      // keys of one (batch, head) contiguous (the materialised non-absorbed K and V)
   float headroom;
   float qscale;         // softmax_scale * log2(e), applied to the fp32 scores
   void* out;            // [B, n_q, H, 128]
