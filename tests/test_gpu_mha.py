@@ -135,6 +135,17 @@ def test_expanded_dc(d_c):
     assert_g2(_expanded(mla, wl, inp, out_dtype=torch.float32), _latent_oracle(wl, inp), f"dc{d_c}")
 
 
+def test_expanded_samples_not_aligned_to_wavefronts():
+    """K_h and V_h are head-major: the rows of one wavefront's 32 tokens are
+    contiguous only within one sample.  With 35-token frames (n_k = 280) and
+    three samples, wavefronts of the expansion straddle sample boundaries."""
+    mla = need_gpu()
+    wl = replace(synth.TINY, name="ragged_samples", batch=3, grid_hw=(5, 7))
+    inp = synth.attend_inputs(wl, seed=4, capacity=wl.n_k + 3)
+    assert wl.n_k % 32 != 0
+    assert_g2(_expanded(mla, wl, inp, out_dtype=torch.float32), _latent_oracle(wl, inp), "straddling samples")
+
+
 def test_expanded_agrees_with_absorbed():
     """Both forms of the same chunk step, side by side, each within the gate of the oracle."""
     mla = need_gpu()
