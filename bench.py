@@ -35,18 +35,28 @@ METRIC = "MLA chunk-attention TFLOP/s + ms/chunk (480P, d_c=192); % bf16 MFMA pe
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 HBM_PEAK_GBS = 8000.0
 COPY_BYTES = 1 << 30           # calibration copy of the traffic probe
-ATTEND_SOURCES = ("latent_kv_cache_chunk_amd/csrc/attend.hip", "latent_kv_cache_chunk_amd/csrc/mla_common.h")
+# sources of the attention kernel that runs at a given latent width
+ATTEND_SOURCES = {
+    "attend_bf16_kernel": ("latent_kv_cache_chunk_amd/csrc/attend.hip", "latent_kv_cache_chunk_amd/csrc/mla_common.h"),
+    "attend_wide_bf16_kernel": ("latent_kv_cache_chunk_amd/csrc/attend_wide.hip",
+                                "latent_kv_cache_chunk_amd/csrc/mla_common.h"),
+}
 
 
-def kernel_source_hash() -> str:
+def attend_kernel(d_c: int) -> str:
+    """The attention kernel of latent width d_c (d_c = 256 runs the single-role kernel)."""
+    return "attend_wide_bf16_kernel" if d_c > 192 else "attend_bf16_kernel"
+
+
+def kernel_source_hash(d_c: int = 192) -> str:
     h = hashlib.sha256()
-    for p in ATTEND_SOURCES:
+    for p in ATTEND_SOURCES[attend_kernel(d_c)]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, d_c: int):
     """HBM bytes per attend launch from committed rocprofv3 counters (written by
     latent_kv_cache_chunk_amd.profile_summary), if the kernel source is unchanged."""
     path = os.path.join(ROOT, "profiles", f"attend_traffic_{workload}.json")
@@ -54,7 +64,7 @@ def load_traffic(workload: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(d_c):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -228,7 +238,7 @@ def main(argv=None) -> int:
     core_flops = wl.attend_core_flops()
     value = step_flops / (ms_step * 1e-3) / 1e12
     attend_tflops = core_flops / (attend_ms * 1e-3) / 1e12
-    traffic = load_traffic(wl.name)
+    traffic = load_traffic(wl.name, wl.d_c)
 
     res = {
         "metric": METRIC,
@@ -252,9 +262,10 @@ def main(argv=None) -> int:
                          "attend": round(attend_ms, 4), "attend_median": round(attend_ms_median, 4),
                          "upproj_merge": round(upproj_ms, 4)},
         "mha_equiv_tflops": round(wl.mha_equiv_flops() / (ms_step * 1e-3) / 1e12, 2),
-        "roofline": {"kernel": "attend_bf16_kernel", "bound": "mfma",
+        "roofline": {"kernel": attend_kernel(wl.d_c), "bound": "mfma",
                      "achieved": round(attend_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attend_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "traffic_gb_s": round(traffic / (attend_ms * 1e-3) / 1e9, 1) if traffic else None,
                      "flop_per_launch": core_flops,
                      "per_unit": f"{4 * wl.d_c + 2 * wl.d_r} flop per visible (row, key); "
                                  f"{wl.batch * wl.n_heads * wl.visible_keys()} visible pairs per launch "

@@ -76,12 +76,15 @@ def _pick(per, pattern: str):
 def cmd_traffic(a) -> None:
     sys.path.insert(0, ROOT)
     import bench
+    from latent_kv_cache_chunk_amd import synth
+    d_c = synth.WORKLOADS[a.workload].d_c
     fetch = _counter(a.fetch, "FETCH_SIZE")
     write = _counter(a.write, "WRITE_SIZE")
     _, f_copy = _pick(fetch, r"neg")
     _, w_copy = _pick(write, r"neg")
-    name, f_att = _pick(fetch, r"attend_bf16_kernel")
-    _, w_att = _pick(write, r"attend_bf16_kernel")
+    pattern = r"mla::(wide::)?" + bench.attend_kernel(d_c)
+    name, f_att = _pick(fetch, pattern)
+    _, w_att = _pick(write, pattern)
     kib = 1024.0
     copy_bytes = float(a.copy_bytes)
     f_scale = copy_bytes / (sum(f_copy) / len(f_copy) * kib)
@@ -90,7 +93,7 @@ def cmd_traffic(a) -> None:
     w_b = sum(w_att) / len(w_att) * kib * w_scale
     out = {
         "kernel": short_name(name), "workload": a.workload,
-        "kernel_source_hash": bench.kernel_source_hash(),
+        "kernel_source_hash": bench.kernel_source_hash(d_c),
         "hbm_bytes_per_launch": round(f_b + w_b),
         "fetch_bytes_per_launch": round(f_b), "write_bytes_per_launch": round(w_b),
         "fetch_scale": f_scale, "write_scale": w_scale,
