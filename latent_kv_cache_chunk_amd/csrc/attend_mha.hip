@@ -607,7 +607,7 @@ MhaPlan make_mha_plan(int B, int H, int n_q, int n_k, int dqk, bool expanded) {
   p.off_k = align_up(p.off_ml + slots * kRowsPerBlock * 2 * 4, 256);
   p.off_v = p.off_k;
   p.total = p.off_k;
-  if (expanded) {   // materialised per-head K [B, n_k, H, dqk] and V [B, n_k, H, 128]
+  if (expanded) {   // materialised per-head K [B, H, n_k, dqk] and V [B, H, n_k, 128] (head major)
     p.off_v = align_up(p.off_k + (int64_t)B * n_k * H * dqk * 2, 256);
     p.total = align_up(p.off_v + (int64_t)B * n_k * H * mha::kDV * 2, 256);
   }
