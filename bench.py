@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA chunk-attention TFLOP/s + ms/chunk (480P, d_c=192); % bf16 MFMA peak"
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 HBM_PEAK_GBS = 8000.0
+HBM_PEAK_BYTES_S = HBM_PEAK_GBS * 1e9
 COPY_BYTES = 1 << 30           # calibration copy of the traffic probe
 # sources of the attention kernel that runs at a given latent width
 ATTEND_SOURCES = {
@@ -163,6 +164,9 @@ def main(argv=None) -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the dense per-head K/V and non-absorbed comparison timings")
+    ap.add_argument("--cold", action="store_true",
+                    help="flush L2 and the last-level cache with a 512 MB write before every timed step; "
+                         "ms_per_step is then the sum of the step's kernel times")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for rocprofv3 --pmc runs: a plain copy of known size, then a few steps; no timing")
     args = ap.parse_args(argv)
@@ -223,14 +227,17 @@ def main(argv=None) -> int:
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)   # evicts the latent cache and q from L2 and the 256 MB last-level cache
         step(evs[i])
     stop.record()
     torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
     per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])   # [steps, 4]
+    ms_step = start.elapsed_time(stop) / args.steps if flush is None else float(np.mean(per.sum(axis=1)))
     append_ms, absorb_ms, attend_ms, upproj_ms = (float(np.mean(per[:, j])) for j in range(4))
     attend_ms_median = float(np.median(per[:, 2]))
 
@@ -239,6 +246,7 @@ def main(argv=None) -> int:
     value = step_flops / (ms_step * 1e-3) / 1e12
     attend_tflops = core_flops / (attend_ms * 1e-3) / 1e12
     traffic = load_traffic(wl.name, wl.d_c)
+    minb = wl.min_hbm_bytes()
 
     res = {
         "metric": METRIC,
@@ -262,10 +270,18 @@ def main(argv=None) -> int:
                          "attend": round(attend_ms, 4), "attend_median": round(attend_ms_median, 4),
                          "upproj_merge": round(upproj_ms, 4)},
         "mha_equiv_tflops": round(wl.mha_equiv_flops() / (ms_step * 1e-3) / 1e12, 2),
+        "cache_state": "cold (512 MB flush before every step)" if args.cold else "hot",
+        "min_hbm": {"step_bytes": sum(minb.values()),
+                    "step_gb_s": round(sum(minb.values()) / (ms_step * 1e-3) / 1e9, 1),
+                    "step_frac_of_8tb_s": round(sum(minb.values()) / (ms_step * 1e-3) / HBM_PEAK_BYTES_S, 4),
+                    "append_bytes": minb["append"],
+                    "append_gb_s": round(minb["append"] / (append_ms * 1e-3) / 1e9, 1)},
         "roofline": {"kernel": attend_kernel(wl.d_c), "bound": "mfma",
                      "achieved": round(attend_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attend_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "traffic_gb_s": round(traffic / (attend_ms * 1e-3) / 1e9, 1) if traffic else None,
+                     "traffic_frac_of_8tb_s": round(traffic / (attend_ms * 1e-3) / HBM_PEAK_BYTES_S, 4)
+                     if traffic else None,
                      "flop_per_launch": core_flops,
                      "per_unit": f"{4 * wl.d_c + 2 * wl.d_r} flop per visible (row, key); "
                                  f"{wl.batch * wl.n_heads * wl.visible_keys()} visible pairs per launch "

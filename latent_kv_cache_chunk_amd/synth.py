@@ -111,6 +111,16 @@ class Workload:
         """Flops of materialising K_h = W_UK[h] c and V_h = W_UV[h] c for every key."""
         return 4.0 * self.batch * self.n_k * self.n_heads * self.head_dim * self.d_c
 
+    def min_hbm_bytes(self) -> dict:
+        """Bytes one step must move at least (every tensor read or written once):
+        append reads x and the two weights and writes the new rows; attention reads
+        the latent cache, q, q_r, W_UK and W_UV and writes the output (bf16)."""
+        w = self.d_c + self.d_r
+        append = 2 * (self.batch * self.n_q * self.d_model + self.d_model * w + self.batch * self.n_q * w)
+        attend = 2 * (self.batch * self.n_k * w + self.batch * self.n_q * self.n_heads * (2 * self.head_dim + self.d_r)
+                      + 2 * self.n_heads * self.head_dim * self.d_c)
+        return {"append": append, "attend": attend}
+
     def append_flops(self) -> float:
         return 2.0 * self.batch * self.n_q * self.d_model * (self.d_c + self.d_r)
 
