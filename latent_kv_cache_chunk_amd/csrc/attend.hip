@@ -33,8 +33,8 @@
 // loads (no registers), one row per key padded to an odd number of 16-byte
 // slots so b128 reads of 16 consecutive rows hit distinct banks.  In step k
 // the score wavefronts work on tile k, the value wavefronts on tile k-1 (with
-// the P of step k-1), and tile k+1 is in flight: three key buffers, two P
-// buffers, one barrier per step.
+// the P of step k-1), and tile k+1 is in flight (its loads issued by the
+// value wavefronts): three key buffers, two P buffers, one barrier per step.
 //
 // Softmax without rescaling.  The accumulators are never rescaled.  Each
 // row's reference max m is fixed by the first 32-key block of a segment and
