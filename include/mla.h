@@ -266,7 +266,10 @@ int32_t mla_chunk_attend_auto(const mla_dims* dims, int32_t in_dtype, int32_t ou
  * oldest window chunk leaves when chunk j-1 is committed.  The key range of
  * every step is slots [0, n_k), in slot order; attention does not depend on
  * key order and positional keys keep their absolute positions, so nothing
- * is moved.  All batch samples advance together. */
+ * is moved.  All batch samples of one ring advance together; samples at
+ * different rollout positions keep one ring each and are attended one call
+ * per sample (batch 1) over their own slice of the cache, which starts at
+ * element b * capacity * (d_c + d_r). */
 typedef struct mla_ring {
   int32_t chunk_tokens;
   int32_t sink_chunks;
