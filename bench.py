@@ -167,6 +167,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cold", action="store_true",
                     help="flush L2 and the last-level cache with a 512 MB write before every timed step; "
                          "ms_per_step is then the sum of the step's kernel times")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from one captured HIP graph (graph_ms_per_step)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for rocprofv3 --pmc runs: a plain copy of known size, then a few steps; no timing")
     args = ap.parse_args(argv)
@@ -241,6 +243,29 @@ def main(argv=None) -> int:
     append_ms, absorb_ms, attend_ms, upproj_ms = (float(np.mean(per[:, j])) for j in range(4))
     attend_ms_median = float(np.median(per[:, 2]))
 
+    graph_ms = None
+    if args.graph:
+        # the same step captured once; launch-bound small steps pay one graph launch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+
     step_flops = wl.attend_flops() + wl.append_flops()
     core_flops = wl.attend_core_flops()
     value = step_flops / (ms_step * 1e-3) / 1e12
@@ -271,6 +296,7 @@ def main(argv=None) -> int:
                          "upproj_merge": round(upproj_ms, 4)},
         "mha_equiv_tflops": round(wl.mha_equiv_flops() / (ms_step * 1e-3) / 1e12, 2),
         "cache_state": "cold (512 MB flush before every step)" if args.cold else "hot",
+        "graph_ms_per_step": round(graph_ms, 4) if graph_ms is not None else None,
         "min_hbm": {"step_bytes": sum(minb.values()),
                     "step_gb_s": round(sum(minb.values()) / (ms_step * 1e-3) / 1e9, 1),
                     "step_frac_of_8tb_s": round(sum(minb.values()) / (ms_step * 1e-3) / HBM_PEAK_BYTES_S, 4),
