@@ -47,6 +47,8 @@ class Workload:
     theta: float = 1e4
     d_model: int = 1536
     chunk_tokens: int = 0             # > 0: queries span chunks of this many tokens (block-causal)
+    query_tokens: int = 0             # > 0: only the chunk's first query_tokens tokens are queries (one GPU's
+                                      # share of a query-sharded step); the keys still hold the whole chunk
     notes: str = field(default="", compare=False)
 
     @property
@@ -54,8 +56,13 @@ class Workload:
         return self.grid_hw[0] * self.grid_hw[1]
 
     @property
-    def n_q(self) -> int:
+    def chunk_len_tokens(self) -> int:
+        """Tokens of the current chunk's frames (all appended before attention)."""
         return len(self.query_frames) * self.frame_tokens
+
+    @property
+    def n_q(self) -> int:
+        return self.query_tokens or self.chunk_len_tokens
 
     @property
     def n_cached(self) -> int:
@@ -63,7 +70,11 @@ class Workload:
 
     @property
     def n_k(self) -> int:
-        return self.n_cached + self.n_q
+        return self.n_cached + self.chunk_len_tokens
+
+    def query_positions(self) -> np.ndarray:
+        """(t, y, x) of the query tokens, in token order."""
+        return chunk_positions(self.query_frames, self.grid_hw)[:self.n_q]
 
     @property
     def scale(self) -> float:
@@ -134,6 +145,9 @@ TINY = Workload("tiny", 1, (4, 6), _frames(0, 6), _frames(6, 8),
 WAN480P = Workload("wan480p", 1, (30, 52), _frames(0, 18), _frames(18, 21),
                    notes="frame 30x52, chunk 3 frames (4680 queries), 6 cached chunks")
 WAN480P_B8 = replace(WAN480P, batch=8, name="wan480p_b8")
+WAN480P_SHARD8 = replace(WAN480P, name="wan480p_shard8", query_tokens=4680 // 8,
+                         notes="one GPU's share of an 8-way query-sharded 480P step: 585 of the chunk's "
+                               "4680 queries against all 32760 keys")
 WAN720P_LONG = Workload("wan720p_long", 1, (45, 80),
                         _frames(0, 3) + _frames(219, 237), _frames(237, 240),
                         notes="frame 45x80, chunk 3 frames (10800 queries), "
@@ -144,7 +158,7 @@ DC_SWEEP = tuple(WAN480P.with_dc(d) for d in (64, 128, 192, 256))
 WAN480P_TF = Workload("wan480p_tf", 1, (30, 52), (), _frames(0, 21), chunk_tokens=3 * 30 * 52,
                       notes="7 chunks of 4680 queries, block-causal")
 
-WORKLOADS = {w.name: w for w in (TINY, WAN480P, WAN480P_B8, WAN720P_LONG, WAN480P_TF) + DC_SWEEP}
+WORKLOADS = {w.name: w for w in (TINY, WAN480P, WAN480P_B8, WAN480P_SHARD8, WAN720P_LONG, WAN480P_TF) + DC_SWEEP}
 
 
 def chunk_positions(frames, grid_hw) -> np.ndarray:
@@ -196,7 +210,7 @@ def attend_inputs(wl: Workload, seed: int = 0, dtype: torch.dtype = torch.bfloat
     return dict(
         cache=_to(cache, dtype), q=_to(q, dtype), q_r=_to(q_r, dtype),
         w_uk=_to(w_uk, dtype), w_uv=_to(w_uv, dtype),
-        q_pos=torch.from_numpy(chunk_positions(wl.query_frames, wl.grid_hw)),
+        q_pos=torch.from_numpy(wl.query_positions()),
         n_k=wl.n_k, scale=wl.scale,
     )
 
@@ -230,7 +244,7 @@ def append_inputs(wl: Workload, seed: int = 0, dtype: torch.dtype = torch.bfloat
         x[b] = _normal(_rng(1000 + b + 7919 * seed + 500000), x.shape[1:])
     return dict(
         x=_to(x, dtype), w_dkv=_to(w_dkv, dtype), w_kr=_to(w_kr, dtype),
-        pos=torch.from_numpy(chunk_positions(wl.query_frames, wl.grid_hw)),
+        pos=torch.from_numpy(wl.query_positions()),
     )
 
 

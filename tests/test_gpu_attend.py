@@ -161,7 +161,7 @@ def test_max_key_at_tile_edges():
 
 
 # ---------------------------------------------------- full workload shapes
-@pytest.mark.parametrize("name", ["wan480p", "wan720p_long"])
+@pytest.mark.parametrize("name", ["wan480p", "wan720p_long", "wan480p_shard8"])
 def test_full_shape_sampled_rows(name):
     mla = need_gpu()
     wl = synth.WORKLOADS[name]
