@@ -21,7 +21,10 @@
 // The score wavefront never holds O and the value wavefront never holds q~,
 // so each fits its registers with room to spare, and while one wavefront of
 // a SIMD is in its softmax the other keeps the matrix core busy.  Each LDS
-// operand read feeds two MFMAs (the group's two 32-row halves).
+// operand read feeds two MFMAs (the group's two 32-row halves).  At d_c <= 64
+// the scores are cheap against the softmax, so each half gets a score
+// wavefront of its own (three wavefronts per SIMD): the exponentials of a
+// group then run in two wavefronts beside the value wavefront's MFMAs.
 //
 // With keys on the MFMA rows one lane holds 16 keys of one row, so row sums
 // are lane-local.  Lane-half h of the S^T accumulator holds keys
@@ -56,9 +59,14 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ inline void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0), others free
 
-constexpr int kWaves = 8;          // wavefronts per workgroup
-constexpr int kGroups = 4;         // row groups (score + value wavefront each)
+constexpr int kGroups = 4;         // row groups (score + value wavefronts each)
 constexpr int kGroupRows = 64;     // rows per group: two 32-row MFMA blocks
+// 32-row halves per score wavefront: at d_c <= 64 each group has two score
+// wavefronts, one per half, so the softmax of a group runs in two wavefronts
+// beside the value wavefront (three per SIMD; the value accumulators of 64
+// rows x d_c columns still fit the third of the register file each gets).
+template <int DC> constexpr int score_halves() { return DC <= 64 ? 1 : 2; }
+template <int DC> constexpr int attend_waves() { return kGroups * (score_halves<DC>() == 1 ? 3 : 2); }
 static_assert(kGroups * kGroupRows == kRowsPerBlock, "a workgroup covers one row block");
 
 template <int DC>
@@ -97,7 +105,8 @@ struct SweepCtx {
   const char* gbase;   // cache rows of this sample
   int n_k;
   bool causal;         // keys limited per row (chunk-causal visibility)
-  int kv[2];           // score lanes: visible keys of the lane's row in each half
+  int kv[2];           // score lanes: visible keys of the lane's row in each of the wavefront's halves
+  int qb0;             // score wavefronts: first 32-row half of the group they cover
   int kv_min;          // score wavefronts: smallest kv of the wavefront
   int wave, lane, half, group;
   int lane_chunk, lane_row;
@@ -160,9 +169,10 @@ __device__ __forceinline__ float block_max(const f32x16& s) {
 // ---------------------------------------------------------------- score role
 template <int DC>
 struct ScoreState {
-  bf16x8 qf[2][AttendTile<DC>::KS];   // absorbed queries of the group's two halves (MFMA B operands)
-  float m_ref[2];                     // reference max (base 2), identical in lanes l and l^32
-  float l_run[2];                     // this lane's part of the running sum
+  static constexpr int NQB = score_halves<DC>();
+  bf16x8 qf[NQB][AttendTile<DC>::KS];   // absorbed queries of the wavefront's halves (MFMA B operands)
+  float m_ref[NQB];                     // reference max (base 2), identical in lanes l and l^32
+  float l_run[NQB];                     // this lane's part of the running sum
 };
 
 constexpr int kScorePrefetch = 4;     // score operand loads in flight ahead of their MFMAs
@@ -172,13 +182,15 @@ template <int DC, Pass P>
 __device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile, char* pbuf, int t, bool first_tile,
                                            const SweepCtx& c) {
   using L = AttendTile<DC>;
-  constexpr int KS = L::KS, PF = kScorePrefetch;
+  constexpr int KS = L::KS, PF = kScorePrefetch, NQB = ScoreState<DC>::NQB;
   const int left = c.n_k - t * L::BN;
 #pragma unroll
   for (int kb = 0; kb < L::NBLK; ++kb) {
     if (kb > 0 && kb * 32 >= left) break;
     const char* kbase = tile + kb * 32 * L::ROWB + c.s_off;
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    f32x16 s[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) s[qb] = f32x16{};
     bf16x8 a[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) a[i] = *reinterpret_cast<const bf16x8*>(kbase + i * 32);
@@ -186,21 +198,21 @@ __device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile,
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 cur = a[ks % PF];
       if (ks + PF < KS) a[ks % PF] = *reinterpret_cast<const bf16x8*>(kbase + (ks + PF) * 32);
-      s[0] = mfma_32x32x16(cur, st.qf[0][ks], s[0]);
-      s[1] = mfma_32x32x16(cur, st.qf[1][ks], s[1]);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) s[qb] = mfma_32x32x16(cur, st.qf[qb][ks], s[qb]);
     }
     const int key0 = t * L::BN + kb * 32;
     if (c.causal) {
       if (key0 + 32 > c.kv_min) {   // some row of the wavefront ends inside this block
-        mask_block(s[0], c.kv[0] - key0, c.half);
-        mask_block(s[1], c.kv[1] - key0, c.half);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) mask_block(s[qb], c.kv[qb] - key0, c.half);
       }
     } else if (left - kb * 32 < 32) {
-      mask_block(s[0], left - kb * 32, c.half);
-      mask_block(s[1], left - kb * 32, c.half);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) mask_block(s[qb], left - kb * 32, c.half);
     }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       if (P == Pass::kMax) {
         st.m_ref[qb] = fmaxf(st.m_ref[qb], block_max(s[qb]));
         continue;
@@ -224,7 +236,7 @@ __device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile,
           pv[e] = two[0];
           pv[e + 1] = two[1];
         }
-        *reinterpret_cast<bf16x8*>(pbuf + kb * L::PBLK + p_slot(c.group, qb, part, c.lane)) = pv;
+        *reinterpret_cast<bf16x8*>(pbuf + kb * L::PBLK + p_slot(c.group, (NQB == 1 ? c.qb0 : 0) + qb, part, c.lane)) = pv;
       }
     }
   }
@@ -351,36 +363,42 @@ __device__ __forceinline__ void score_role(SweepCtx& c, SegmentIter it, const u1
                                            const Visibility& vis, char* k0, char* k1, char* k2, char* pb0,
                                            char* pb1) {
   using L = AttendTile<DC>;
+  constexpr int NQB = ScoreState<DC>::NQB;
   ScoreState<DC> st;
   while (it.next()) {
     c.gbase = reinterpret_cast<const char*>(cache + (int64_t)it.b * cache_bstride);
     const int te = visible_end<DC>(it, vis, c.n_k);
     const int64_t row0 = (int64_t)it.b * rows_pad_b + (int64_t)it.rbl * kRowsPerBlock + c.group * kGroupRows;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const u16* qrow = qt + (row0 + qb * 32 + (c.lane & 31)) * L::W + c.half * 8;
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int half_row = ((NQB == 1 ? c.qb0 : 0) + qb) * 32 + (c.lane & 31);
+      const u16* qrow = qt + (row0 + half_row) * L::W + c.half * 8;
 #pragma unroll
       for (int ks = 0; ks < L::KS; ++ks) st.qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
       st.l_run[qb] = 0.f;
       st.m_ref[qb] = -INFINITY;
-      c.kv[qb] = vis.kv_of_row(it.rbl * kRowsPerBlock + c.group * kGroupRows + qb * 32 + (c.lane & 31), c.n_k);
+      c.kv[qb] = vis.kv_of_row(it.rbl * kRowsPerBlock + c.group * kGroupRows + half_row, c.n_k);
     }
-    c.kv_min = wave_min(min(c.kv[0], c.kv[1]));
+    c.kv_min = wave_min(NQB == 2 ? min(c.kv[0], c.kv[1]) : c.kv[0]);
     if (te > it.t0) sweep<DC, Pass::kSingle, true>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
     const float lim = __builtin_amdgcn_exp2f(headroom);
-    const bool over = !(st.l_run[0] <= lim) || !(st.l_run[1] <= lim);
+    bool over = false;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) over |= !(st.l_run[qb] <= lim);
     if (__syncthreads_or(over)) {
       // A running sum rose past 2^headroom: exact two-pass evaluation.
-      st.m_ref[0] = st.m_ref[1] = -INFINITY;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) st.m_ref[qb] = -INFINITY;
       sweep<DC, Pass::kMax, true>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
-      st.l_run[0] = st.l_run[1] = 0.f;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) st.l_run[qb] = 0.f;
       sweep<DC, Pass::kAccum, true>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
     }
     const int64_t slot = seg_slot(w, it.rb);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       const float l_tot = st.l_run[qb] + __shfl_xor(st.l_run[qb], 32);
-      const int rl = c.group * kGroupRows + qb * 32 + (c.lane & 31);
+      const int rl = c.group * kGroupRows + ((NQB == 1 ? c.qb0 : 0) + qb) * 32 + (c.lane & 31);
       if (c.half == 0) {
         part_ml[(slot * kRowsPerBlock + rl) * 2 + 0] = st.m_ref[qb];
         part_ml[(slot * kRowsPerBlock + rl) * 2 + 1] = l_tot;
@@ -440,7 +458,7 @@ __device__ __forceinline__ void value_role(SweepCtx& c, SegmentIter it, const u1
 // units; each row-block segment leaves a partial softmax state (m, l, L) in
 // its slot: score wavefronts write (m, l), value wavefronts write L.
 template <int DC>
-__global__ __launch_bounds__(kWaves * 64, 1)
+__global__ __launch_bounds__(attend_waves<DC>() * 64, 1)
 void attend_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstride, int n_k,
                         const u16* __restrict__ qt, int rows_pad_b, int rb_per_b,
                         float* __restrict__ part_L, float* __restrict__ part_ml,
@@ -460,8 +478,11 @@ void attend_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstride, in
   c.lane = threadIdx.x & 63;
   c.half = c.lane >> 5;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool scorer = c.wave < kGroups;   // wavefronts w and w + 4 share a SIMD
+  // wavefront w runs on SIMD w % 4: group g's wavefronts are g, g + 4 (and g + 8)
+  constexpr int kScoreWaves = kGroups * (3 - score_halves<DC>());
+  const bool scorer = c.wave < kScoreWaves;
   c.group = c.wave & (kGroups - 1);
+  c.qb0 = score_halves<DC>() == 1 ? (c.wave >> 2) & 1 : 0;
   c.lane_chunk = lane_copy_chunk<DC>(c.lane, c.lane_row);
   c.s_off = (c.lane & 31) * L::ROWB + c.half * 16;
   const int g = c.lane >> 4, j = c.lane & 15;
@@ -589,9 +610,9 @@ hipError_t launch_attend_bf16(const Plan& p, const AttendArgs& a, hipStream_t s)
   float* ml = (float*)(ws + p.off_ml);
   const dim3 grid(p.G);
   switch (p.d_c) {
-    case 64: attend_bf16_kernel<64><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom, a.vis, units, p.nrb, hdr); break;
-    case 128: attend_bf16_kernel<128><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom, a.vis, units, p.nrb, hdr); break;
-    case 192: attend_bf16_kernel<192><<<grid, dim3(kWaves * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom, a.vis, units, p.nrb, hdr); break;
+    case 64: attend_bf16_kernel<64><<<grid, dim3(attend_waves<64>() * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom, a.vis, units, p.nrb, hdr); break;
+    case 128: attend_bf16_kernel<128><<<grid, dim3(attend_waves<128>() * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom, a.vis, units, p.nrb, hdr); break;
+    case 192: attend_bf16_kernel<192><<<grid, dim3(attend_waves<192>() * 64), 0, s>>>(cache, a.cache_bstride, p.n_k, qt, p.rows_pad_b, p.rb_per_b, L, ml, p.T, p.U, p.G, a.headroom, a.vis, units, p.nrb, hdr); break;
     case 256: return launch_attend_wide_bf16(p, a, s);   // value accumulators would not fit the role split
     default: return hipErrorInvalidValue;
   }
