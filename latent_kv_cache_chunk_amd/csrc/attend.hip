@@ -21,7 +21,7 @@
 // The score wavefront never holds O and the value wavefront never holds q~,
 // so each fits its registers with room to spare, and while one wavefront of
 // a SIMD is in its softmax the other keeps the matrix core busy.  Each LDS
-// operand read feeds two MFMAs (the group's two 32-row halves).  At d_c <= 64
+// operand read feeds two MFMAs (the group's two 32-row halves).  At d_c <= 128
 // the scores are cheap against the softmax, so each half gets a score
 // wavefront of its own (three wavefronts per SIMD): the exponentials of a
 // group then run in two wavefronts beside the value wavefront's MFMAs.
@@ -61,11 +61,12 @@ __device__ inline void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  //
 
 constexpr int kGroups = 4;         // row groups (score + value wavefronts each)
 constexpr int kGroupRows = 64;     // rows per group: two 32-row MFMA blocks
-// 32-row halves per score wavefront: at d_c <= 64 each group has two score
+// 32-row halves per score wavefront: at d_c <= 128 each group has two score
 // wavefronts, one per half, so the softmax of a group runs in two wavefronts
 // beside the value wavefront (three per SIMD; the value accumulators of 64
-// rows x d_c columns still fit the third of the register file each gets).
-template <int DC> constexpr int score_halves() { return DC <= 64 ? 1 : 2; }
+// rows x d_c columns still fit the third of the register file each gets, with
+// the spills of d_c = 128 confined to segment set-up and epilogue code).
+template <int DC> constexpr int score_halves() { return DC <= 128 ? 1 : 2; }
 template <int DC> constexpr int attend_waves() { return kGroups * (score_halves<DC>() == 1 ? 3 : 2); }
 static_assert(kGroups * kGroupRows == kRowsPerBlock, "a workgroup covers one row block");
 
