@@ -160,10 +160,23 @@ def _check(t: torch.Tensor, name: str, shape, dtype=None):
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, but the library launches on the current device "
+                         f"cuda:{torch.cuda.current_device()}")
+
+
+def _ws(workspace):
+    """(device pointer, size in bytes) of a workspace tensor of any dtype."""
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    _check(workspace, "workspace", tuple(workspace.shape))
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
 def _stream(stream) -> int:
     s = torch.cuda.current_stream() if stream is None else stream
+    if s.device.index != torch.cuda.current_device():
+        raise ValueError(f"stream is on {s.device}, not on the current device cuda:{torch.cuda.current_device()}")
     return s.cuda_stream
 
 
@@ -234,7 +247,7 @@ def chunk_attend(dims: Dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k: int, scale: 
     d = dims.c()
     args = (_dtype_code(dt), _dtype_code(odt), q.data_ptr(), q_r.data_ptr(), q_pos.data_ptr(), n_q,
             w_uk.data_ptr(), w_uv.data_ptr(), cache.data_ptr(), cache.shape[1], int(n_k))
-    tail = (float(scale), out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream))
+    tail = (float(scale), out.data_ptr(), *_ws(workspace), _stream(stream))
     if causal is None:
         code = _lib.mla_chunk_attend(ctypes.byref(d), *args, *tail)
         _raise(code, "mla_chunk_attend")
@@ -249,8 +262,8 @@ def query_absorb(dims: Dims, q, q_r, q_pos, w_uk, scale: float, n_k: int, worksp
     n_q, dt = _attend_checks(dims, q, q_r, q_pos, w_uk, None, None, n_k)
     d = dims.c()
     code = _lib.mla_query_absorb(ctypes.byref(d), _dtype_code(dt), q.data_ptr(), q_r.data_ptr(), q_pos.data_ptr(),
-                                 n_q, w_uk.data_ptr(), float(scale), int(n_k), workspace.data_ptr(),
-                                 workspace.numel(), _stream(stream))
+                                 n_q, w_uk.data_ptr(), float(scale), int(n_k),
+                                 *_ws(workspace), _stream(stream))
     _raise(code, "mla_query_absorb")
 
 
@@ -258,7 +271,7 @@ def latent_attend(dims: Dims, cache, n_q: int, n_k: int, workspace, stream=None,
     _check(cache, "cache", (dims.batch, cache.shape[1], dims.d_c + dims.d_r), cache.dtype)
     d = dims.c()
     args = (_dtype_code(cache.dtype), cache.data_ptr(), cache.shape[1], int(n_q), int(n_k))
-    tail = (workspace.data_ptr(), workspace.numel(), _stream(stream))
+    tail = (*_ws(workspace), _stream(stream))
     if causal is None:
         _raise(_lib.mla_latent_attend(ctypes.byref(d), *args, *tail), "mla_latent_attend")
     else:
@@ -272,8 +285,8 @@ def value_upproj(dims: Dims, w_uv, out, n_q: int, n_k: int, workspace, stream=No
     _check(out, "out", (dims.batch, n_q, dims.n_heads, dims.head_dim), out.dtype)
     d = dims.c()
     code = _lib.mla_value_upproj(ctypes.byref(d), _dtype_code(w_uv.dtype), _dtype_code(out.dtype), int(n_q),
-                                 int(n_k), w_uv.data_ptr(), out.data_ptr(), workspace.data_ptr(),
-                                 workspace.numel(), _stream(stream))
+                                 int(n_k), w_uv.data_ptr(), out.data_ptr(),
+                                 *_ws(workspace), _stream(stream))
     _raise(code, "mla_value_upproj")
 
 
@@ -301,7 +314,7 @@ def mha_attend(q, k, v, n_k: int, scale: float, out=None, out_dtype=None, worksp
     if workspace is None:
         workspace = torch.empty(mha_workspace_bytes(B, H, dh, n_q, n_k), dtype=torch.uint8, device=q.device)
     code = _lib.mla_mha_attend(B, H, dh, _dtype_code(odt), q.data_ptr(), n_q, k.data_ptr(), v.data_ptr(), cap,
-                               int(n_k), float(scale), out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                               int(n_k), float(scale), out.data_ptr(), *_ws(workspace),
                                _stream(stream))
     _raise(code, "mla_mha_attend")
     return out
@@ -332,7 +345,7 @@ def chunk_attend_expanded(dims: Dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k: int
     code = _lib.mla_chunk_attend_expanded(ctypes.byref(d), _dtype_code(odt), q.data_ptr(), q_r.data_ptr(),
                                           q_pos.data_ptr(), n_q, w_uk.data_ptr(), w_uv.data_ptr(), cache.data_ptr(),
                                           cache.shape[1], int(n_k), float(scale), out.data_ptr(),
-                                          workspace.data_ptr(), workspace.numel(), _stream(stream))
+                                          *_ws(workspace), _stream(stream))
     _raise(code, "mla_chunk_attend_expanded")
     return out
 
@@ -366,7 +379,7 @@ def chunk_attend_auto(dims: Dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k: int, sc
     code = _lib.mla_chunk_attend_auto(ctypes.byref(d), _dtype_code(dt), _dtype_code(odt), q.data_ptr(),
                                       q_r.data_ptr(), q_pos.data_ptr(), n_q, w_uk.data_ptr(), w_uv.data_ptr(),
                                       cache.data_ptr(), cache.shape[1], int(n_k), float(scale), out.data_ptr(),
-                                      workspace.data_ptr(), workspace.numel(), _stream(stream))
+                                      *_ws(workspace), _stream(stream))
     _raise(code, "mla_chunk_attend_auto")
     return out
 

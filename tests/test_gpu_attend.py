@@ -259,3 +259,20 @@ def test_two_pass_fallback(monkeypatch, headroom):
     want = _oracle(wl, inp)
     assert_g1(_gpu(mla, wl, inp), want, "two-pass bf16")
     assert_g2(_gpu(mla, wl, inp, out_dtype=torch.float32), want, "two-pass f32 out")
+
+
+def test_workspace_of_any_dtype_and_host_workspace_rejected():
+    """The binding passes the workspace's size in bytes, whatever its dtype, and
+    rejects a host tensor before anything is launched."""
+    mla = need_gpu()
+    wl = replace(synth.TINY, grid_hw=(30, 10), query_frames=(6,), cache_frames=tuple(range(6)))
+    inp = synth.attend_inputs(wl, seed=13)
+    d = _dims(mla, wl)
+    n = mla.workspace_bytes(d, torch.bfloat16, wl.n_q, wl.n_k)
+    a = _gpu(mla, wl, inp, workspace=mla.alloc_workspace(d, torch.bfloat16, wl.n_q, wl.n_k))
+    b = _gpu(mla, wl, inp, workspace=torch.empty((n + 3) // 4, dtype=torch.float32, device="cuda"))
+    assert np.array_equal(a, b)
+    with pytest.raises(ValueError, match="workspace"):
+        _gpu(mla, wl, inp, workspace=torch.empty(n, dtype=torch.uint8))
+    with pytest.raises(mla.MLAError):
+        _gpu(mla, wl, inp, workspace=torch.empty(n // 2, dtype=torch.uint8, device="cuda"))
