@@ -228,3 +228,31 @@ def test_binding_checks_tensors_on_host():
         mla.cache_append(d, torch.zeros(1, 4, 64, dtype=torch.bfloat16), torch.zeros(192, 64, dtype=torch.bfloat16),
                          torch.zeros(32, 64, dtype=torch.bfloat16), torch.zeros(4, 3, dtype=torch.int32),
                          torch.zeros(1, 8, 224, dtype=torch.bfloat16), 0)
+
+
+def test_last_error_is_per_thread():
+    """Validation messages are kept per thread: two threads failing different
+    checks at the same time each read back their own message."""
+    import threading
+    lib = mla.raw()
+    fake = ctypes.c_void_p(0x10000)
+    seen = {"null": [], "capacity": []}
+
+    def worker(kind, n):
+        d = _dims()
+        for _ in range(n):
+            if kind == "null":
+                rc = lib.mla_chunk_attend(ctypes.byref(d), 0, 0, None, fake, fake, 48, fake, fake, fake, 192, 192,
+                                          ctypes.c_float(0.08), fake, fake, 1 << 40, None)
+            else:
+                rc = lib.mla_chunk_attend(ctypes.byref(d), 0, 0, fake, fake, fake, 48, fake, fake, fake, 100, 192,
+                                          ctypes.c_float(0.08), fake, fake, 1 << 40, None)
+            seen[kind].append((rc, lib.mla_last_error()))
+
+    threads = [threading.Thread(target=worker, args=(k, 2000)) for k in ("null", "capacity")]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert all(rc == -1 and b"q is null" in m for rc, m in seen["null"])
+    assert all(rc == -1 and b"capacity" in m for rc, m in seen["capacity"])
