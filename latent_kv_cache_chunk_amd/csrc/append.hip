@@ -62,6 +62,25 @@ void append_bf16_kernel(const u16* __restrict__ x, int D, int ntok, int n_new,
   const int tok0 = tb * 32;
   const int n_base = nb * 32;
 
+  // The epilogue's rotation depends only on positions, so the workgroups of
+  // the positional block evaluate it (fp64 angles, then cos and sin) before
+  // their k loop: its latency then overlaps the loads of the CU's other
+  // workgroups instead of extending this workgroup's tail.  Thread mapping as
+  // in the epilogue (token tid / 8, outputs n_base + (tid % 8) * 4 .. + 3).
+  float rc0 = 1.f, rs0 = 0.f, rc1 = 1.f, rs1 = 0.f;
+  if (n_base + 32 > d_c) {
+    const int et = threadIdx.x >> 3, enn = n_base + (threadIdx.x & 7) * 4;
+    if (enn >= d_c) {
+      const int ei = min(tok0 + et, ntok - 1) % n_new;
+      const int pt = pos[3 * ei], ph = pos[3 * ei + 1], pw = pos[3 * ei + 2];
+      const int pair = (enn - d_c) >> 1;
+      const double a0 = rope_angle(pair, pt, ph, pw, rope);
+      const double a1 = rope_angle(pair + 1, pt, ph, pw, rope);
+      rc0 = (float)cos(a0); rs0 = (float)sin(a0);
+      rc1 = (float)cos(a1); rs1 = (float)sin(a1);
+    }
+  }
+
   // global row pointers of this lane's four x rows and four W rows (row-major loads)
   const int lrow = lane >> 3, piece = lane & 7;
   const u16* xr[4];
@@ -150,12 +169,7 @@ void append_bf16_kernel(const u16* __restrict__ x, int D, int ntok, int n_new,
   const int b = tok / n_new, i = tok - b * n_new;
   const int nn = n_base + n0;
   if (nn >= d_c) {                                   // positional key: rotate the two pairs
-    const int pt = pos[3 * i], ph = pos[3 * i + 1], pw = pos[3 * i + 2];
-    const int pair = (nn - d_c) >> 1;
-    const double a0 = rope_angle(pair, pt, ph, pw, rope);
-    const double a1 = rope_angle(pair + 1, pt, ph, pw, rope);
-    const float c0 = (float)cos(a0), s0 = (float)sin(a0);
-    const float c1 = (float)cos(a1), s1 = (float)sin(a1);
+    const float c0 = rc0, s0 = rs0, c1 = rc1, s1 = rs1;
     const float r0 = fmaf(v[0], c0, -(v[1] * s0)), r1 = fmaf(v[0], s0, v[1] * c0);
     const float r2 = fmaf(v[2], c1, -(v[3] * s1)), r3 = fmaf(v[2], s1, v[3] * c1);
     v = f32x4{r0, r1, r2, r3};
