@@ -27,20 +27,24 @@ def errors(got: np.ndarray, want: np.ndarray) -> dict:
 #   G1 raw absolute error of the bf16 output on unit-scale values
 G1_MAX, G1_MEAN = 2e-2, 2e-3
 #   G2 error of the fp32-output path divided by the RMS of the reference output.
-#   Mean 2e-3.  Max 3e-2: emulating in fp64 only the roundings any bf16 MFMA
-#   path must make (absorbed query and P rounded once to bf16, L in fp32)
-#   gives normalised max errors of 0.010-0.016 against the oracle with the
-#   exact running max and 0.015-0.021 with the first-block reference max the
-#   kernel uses (rows dominated by one key no longer get p = 1 exactly), at
-#   148-key shapes for d_c 64 and 192 over three seeds; mean errors 1.5-1.7e-3
-#   either way.
-G2_MAX, G2_MEAN = 3e-2, 2e-3
-#   Chunk-causal calls include rows that see only one chunk (down to a single
-#   key), where the bf16 roundings of q~ and P are not averaged over many keys.
-#   The same fp64 emulation on the tiny causal shapes (chunk 1, 48, 50; three
-#   seeds) gives normalised max errors of 0.019-0.041 and means of
-#   1.25-1.65e-3, so the max gate for these calls is 5e-2 (mean unchanged).
-G2_CAUSAL_MAX = 5e-2
+#   The bounds come from tests/test_tolerances.py, which models the roundings
+#   of the bf16 path (q~ and P rounded once to bf16, fp32 accumulation, L kept
+#   as a bf16 hi/lo pair) on the inputs of every G2 case and asserts each gate
+#   sits at least 15% above the modelled floor and at most 50% above it:
+#     * rows that see whole key ranges: 1.4-1.5e-2 with the exact running max,
+#       up to 2.12e-2 with the first-32-key reference max the fused kernels use
+#       (a key above it gets p > 1, rounded like any p; with the exact max the
+#       dominant key's p = 1 is exact) -> max 2.5e-2;
+#     * chunk-causal calls and calls with fewer than 148 keys, whose rows can
+#       see a single chunk down to one key: up to 3.0e-2 even with the exact
+#       max -> max 4e-2;
+#     * mean errors 1.2-1.65e-3 everywhere -> mean 2e-3.
+G2_MAX, G2_MEAN = 2.5e-2, 2e-3
+G2_CAUSAL_MAX = 4e-2
+#   The non-absorbed form rounds the materialised per-head K_h and V_h to bf16
+#   as well: modelled floors up to 2.95e-2 (max) and 1.99e-3 (mean) on its
+#   test inputs, any key count -> max 3.5e-2, mean 2.5e-3.
+G2X_MAX, G2X_MEAN = 3.5e-2, 2.5e-3
 #   fp32 inputs, fp32 output, divided by the RMS of the reference output
 F32_MAX, F32_MEAN = 1e-4, 1e-5
 
@@ -52,11 +56,16 @@ def assert_g1(got, want, label=""):
     return e
 
 
-def assert_g2(got, want, label="", max_norm=G2_MAX):
+def assert_g2(got, want, label="", max_norm=G2_MAX, mean_norm=G2_MEAN):
     e = errors(got, want)
     assert np.all(np.isfinite(got)), label
-    assert e["max_norm"] <= max_norm and e["mean_norm"] <= G2_MEAN, (label, e)
+    assert e["max_norm"] <= max_norm and e["mean_norm"] <= mean_norm, (label, e)
     return e
+
+
+def assert_g2x(got, want, label=""):
+    """G2 for the non-absorbed form (one more bf16 rounding: K_h and V_h)."""
+    return assert_g2(got, want, label, max_norm=G2X_MAX, mean_norm=G2X_MEAN)
 
 
 def assert_f32(got, want, label=""):

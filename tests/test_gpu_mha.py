@@ -22,7 +22,7 @@ import torch
 
 import oracle
 from latent_kv_cache_chunk_amd import synth
-from tests.gpu_util import assert_g1, assert_g2, need_gpu, np64
+from tests.gpu_util import assert_g1, assert_g2, assert_g2x, need_gpu, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -124,7 +124,7 @@ def test_expanded_tiny_bf16_and_f32_out():
     inp = synth.attend_inputs(wl, seed=0, capacity=wl.n_k + 9)
     want = _latent_oracle(wl, inp)
     assert_g1(_expanded(mla, wl, inp), want, "bf16 out")
-    assert_g2(_expanded(mla, wl, inp, out_dtype=torch.float32), want, "f32 out")
+    assert_g2x(_expanded(mla, wl, inp, out_dtype=torch.float32), want, "f32 out")
 
 
 @pytest.mark.parametrize("d_c", [64, 128, 192, 256])
@@ -132,7 +132,7 @@ def test_expanded_dc(d_c):
     mla = need_gpu()
     wl = replace(synth.TINY, batch=2).with_dc(d_c)
     inp = synth.attend_inputs(wl, seed=1)
-    assert_g2(_expanded(mla, wl, inp, out_dtype=torch.float32), _latent_oracle(wl, inp), f"dc{d_c}")
+    assert_g2x(_expanded(mla, wl, inp, out_dtype=torch.float32), _latent_oracle(wl, inp), f"dc{d_c}")
 
 
 def test_expanded_samples_not_aligned_to_wavefronts():
@@ -143,7 +143,7 @@ def test_expanded_samples_not_aligned_to_wavefronts():
     wl = replace(synth.TINY, name="ragged_samples", batch=3, grid_hw=(5, 7))
     inp = synth.attend_inputs(wl, seed=4, capacity=wl.n_k + 3)
     assert wl.n_k % 32 != 0
-    assert_g2(_expanded(mla, wl, inp, out_dtype=torch.float32), _latent_oracle(wl, inp), "straddling samples")
+    assert_g2x(_expanded(mla, wl, inp, out_dtype=torch.float32), _latent_oracle(wl, inp), "straddling samples")
 
 
 def test_expanded_agrees_with_absorbed():
@@ -160,7 +160,7 @@ def test_expanded_agrees_with_absorbed():
     want = oracle.chunk_attend_rows(rows, np64(inp["q"]), np64(inp["q_r"]), inp["q_pos"].numpy(), np64(inp["w_uk"]),
                                     np64(inp["w_uv"]), np64(inp["cache"]), wl.n_k, wl.scale)
     assert_g2(a[rows[:, 0], rows[:, 1], rows[:, 2]], want, "absorbed")
-    assert_g2(e[rows[:, 0], rows[:, 1], rows[:, 2]], want, "expanded")
+    assert_g2x(e[rows[:, 0], rows[:, 1], rows[:, 2]], want, "expanded")
 
 
 def test_expanded_480p_sampled_rows():
@@ -173,7 +173,7 @@ def test_expanded_480p_sampled_rows():
     rows = np.stack([np.zeros_like(i), i, rng.integers(0, wl.n_heads, i.size)], 1)
     want = oracle.chunk_attend_rows(rows, np64(inp["q"]), np64(inp["q_r"]), inp["q_pos"].numpy(), np64(inp["w_uk"]),
                                     np64(inp["w_uv"]), np64(inp["cache"]), wl.n_k, wl.scale)
-    assert_g2(got[rows[:, 0], rows[:, 1], rows[:, 2]], want, "480p expanded")
+    assert_g2x(got[rows[:, 0], rows[:, 1], rows[:, 2]], want, "480p expanded")
     assert np.all(np.isfinite(got))
 
 
@@ -209,4 +209,4 @@ def test_auto_long_chunk_runs_the_non_absorbed_form():
     rows = np.stack([np.zeros(40, np.int64), rng.integers(0, wl.n_q, 40), rng.integers(0, wl.n_heads, 40)], 1)
     want = oracle.chunk_attend_rows(rows, np64(inp["q"]), np64(inp["q_r"]), inp["q_pos"].numpy(), np64(inp["w_uk"]),
                                     np64(inp["w_uv"]), np64(inp["cache"]), wl.n_k, wl.scale)
-    assert_g2(np64(b)[rows[:, 0], rows[:, 1], rows[:, 2]], want, "auto long")
+    assert_g2x(np64(b)[rows[:, 0], rows[:, 1], rows[:, 2]], want, "auto long")
