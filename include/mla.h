@@ -279,7 +279,10 @@ typedef struct mla_ring {
 } mla_ring;
 
 /* Initialize an empty ring.  chunk_tokens >= 1, sink_chunks >= 0,
- * window_chunks >= 0. */
+ * window_chunks >= 0.  The struct is plain data owned by the caller and the
+ * library keeps no other state: saving it together with each sample's cache
+ * slots [0, capacity) checkpoints a rollout, and restoring both resumes it
+ * exactly (the next steps write the same slots and attend to the same keys). */
 int32_t mla_ring_init(mla_ring* ring, int32_t chunk_tokens, int32_t sink_chunks, int32_t window_chunks);
 
 /* Where the current chunk goes and which keys its steps attend to: append

@@ -411,6 +411,19 @@ class Ring:
     def commit(self) -> None:
         _raise(_lib.mla_ring_commit(ctypes.byref(self._r)), "mla_ring_commit")
 
+    def state(self) -> tuple:
+        """The ring's whole state (mla_ring is plain caller-owned data): with the
+        cache slots [0, capacity) of its sample it checkpoints the rollout."""
+        r = self._r
+        return (r.chunk_tokens, r.sink_chunks, r.window_chunks, r.capacity, r.committed)
+
+    @classmethod
+    def from_state(cls, state: tuple) -> "Ring":
+        """A ring that resumes from state(): the same slots and n_k from here on."""
+        ring = cls.__new__(cls)
+        ring._r = MlaRing(*(int(v) for v in state))
+        return ring
+
     def slot_chunks(self):
         n = self._r.sink_chunks + self._r.window_chunks + 1
         arr = (_I64 * n)()

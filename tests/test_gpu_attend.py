@@ -4,12 +4,15 @@ against the fp64 non-absorbed oracle, called through the C ABI.
 Gates (unit-scale outputs: the values W_UV c have unit variance under the
 input recipe):
   G1  bf16 output:  raw max |err| <= 2e-2, raw mean |err| <= 2e-3.
-  G2  bf16 inputs, fp32 output: errors divided by RMS(oracle) satisfy the
-      same 2e-2 / 2e-3 (the output of attention is a weighted mean, so its
-      RMS is well below 1 and raw errors alone would be a weak test).
+  G2  bf16 inputs, fp32 output: errors divided by RMS(oracle), max <= 2.5e-2
+      and mean <= 2e-3 (the output of attention is a weighted mean, so its
+      RMS is well below 1 and raw errors alone would be a weak test).  The
+      bounds are derived from a model of the path's bf16 roundings in
+      tests/test_tolerances.py.
   F32 fp32 inputs and output: RMS-normalised max <= 1e-4, mean <= 1e-5.
-Small shapes are compared element by element; the full workload shapes are
-compared on sampled rows that the oracle computes one by one.
+Small shapes and the whole 480P step are compared element by element; the
+other full workload shapes on rows that hit every 256-row block of every
+sample, which the oracle computes one by one.
 """
 
 from dataclasses import replace
@@ -161,12 +164,42 @@ def test_max_key_at_tile_edges():
 
 
 # ---------------------------------------------------- full workload shapes
-@pytest.mark.parametrize("name", ["wan480p", "wan720p_long", "wan480p_shard8"])
-def test_full_shape_sampled_rows(name):
+def _rows_every_block(wl, seed, per_block=1):
+    """Rows (b, i, h) that hit every 256-row block of every sample (rows
+    r = h * n_q + i of a sample are packed 256 to a block, and each block's
+    partial states are merged from the slots of the workgroups that split it),
+    plus the first and last row of every sample."""
+    rng = np.random.default_rng(seed)
+    rows_b = wl.n_heads * wl.n_q
+    out = []
+    for b in range(wl.batch):
+        for r0 in range(0, rows_b, 256):
+            r = rng.integers(r0, min(rows_b, r0 + 256), per_block)
+            out += [[b, int(x) % wl.n_q, int(x) // wl.n_q] for x in r]
+        out += [[b, 0, 0], [b, wl.n_q - 1, wl.n_heads - 1]]
+    return np.array(out, np.int64)
+
+
+def test_480p_every_row():
+    """The headline step (4680 queries x 12 heads over 32760 keys): every one of
+    the 56160 output rows against the oracle, bf16 output under G1 and fp32
+    output under G2."""
+    mla = need_gpu()
+    wl = synth.WAN480P
+    inp = synth.attend_inputs(wl, seed=0)
+    got16 = _gpu(mla, wl, inp)
+    got32 = _gpu(mla, wl, inp, out_dtype=torch.float32)
+    want = _oracle(wl, inp)
+    assert_g1(got16, want, "480p bf16 out, all rows")
+    assert_g2(got32, want, "480p f32 out, all rows")
+
+
+@pytest.mark.parametrize("name", ["wan720p_long", "wan480p_shard8"])
+def test_full_shape_every_row_block(name):
     mla = need_gpu()
     wl = synth.WORKLOADS[name]
     inp = synth.attend_inputs(wl, seed=0)
-    rows = _sample_rows(wl, 96, seed=2, heads=[0, 5, 11])
+    rows = _rows_every_block(wl, seed=2)
     got = _gpu(mla, wl, inp)
     want = _oracle_rows(wl, inp, rows)
     assert_g1(got[rows[:, 0], rows[:, 1], rows[:, 2]], want, name)
@@ -175,25 +208,50 @@ def test_full_shape_sampled_rows(name):
     assert np.all(np.isfinite(got))
 
 
-def test_batched_480p_sampled_rows():
+def test_batched_480p_every_row_block():
+    """Batch 8: 1760 row blocks (220 per sample), each checked on one row."""
     mla = need_gpu()
     wl = synth.WAN480P_B8
     inp = synth.attend_inputs(wl, seed=0)
-    rows = _sample_rows(wl, 64, seed=3, heads=[2, 9])
+    rows = _rows_every_block(wl, seed=3)
     got = _gpu(mla, wl, inp, out_dtype=torch.float32)
     want = _oracle_rows(wl, inp, rows)
     assert_g2(got[rows[:, 0], rows[:, 1], rows[:, 2]], want, "480p b8")
 
 
 @pytest.mark.parametrize("d_c", [64, 128, 256])
-def test_dc_sweep_480p_sampled_rows(d_c):
+def test_dc_sweep_480p_every_row_block(d_c):
     mla = need_gpu()
     wl = synth.WAN480P.with_dc(d_c)
     inp = synth.attend_inputs(wl, seed=0)
-    rows = _sample_rows(wl, 48, seed=4, heads=[1, 7])
+    rows = _rows_every_block(wl, seed=4)
     got = _gpu(mla, wl, inp, out_dtype=torch.float32)
     want = _oracle_rows(wl, inp, rows)
     assert_g2(got[rows[:, 0], rows[:, 1], rows[:, 2]], want, f"480p dc{d_c}")
+
+
+# ------------------------------------------------------- closed forms
+def _mean_of_values(inp, n_k):
+    """q = q_r = 0: every score is 0, so each head's output is the plain mean of
+    its values, O_h = W_UV[h] (mean_j c_j) (closed form; no softmax involved)."""
+    d_c = inp["w_uk"].shape[-1]
+    c_mean = np64(inp["cache"])[:, :n_k, :d_c].mean(axis=1)              # [B, d_c]
+    return np.einsum("bc,hdc->bhd", c_mean, np64(inp["w_uv"]))             # [B, H, d_h]
+
+
+@pytest.mark.parametrize("name", ["stream_k", "wan480p"])
+def test_zero_query_gives_mean_of_values(name):
+    mla = need_gpu()
+    wl = (replace(synth.TINY, grid_hw=(30, 10), query_frames=(6,), cache_frames=tuple(range(6)))
+          if name == "stream_k" else synth.WAN480P)
+    inp = synth.attend_inputs(wl, seed=14)
+    inp["q"] = torch.zeros_like(inp["q"])
+    inp["q_r"] = torch.zeros_like(inp["q_r"])
+    want = np.broadcast_to(_mean_of_values(inp, wl.n_k)[:, None], (wl.batch, wl.n_q, wl.n_heads, wl.head_dim))
+    got = _gpu(mla, wl, inp, out_dtype=torch.float32)
+    # every p is exactly 1 and L the fp32 mean: only the bf16 hi/lo split of L
+    # and the fp32 sums remain, far inside G2
+    assert_g2(got, want, name + " q = 0", max_norm=1e-3, mean_norm=1e-4)
 
 
 # ------------------------------------------------ composition and hygiene

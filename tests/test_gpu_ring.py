@@ -126,3 +126,53 @@ def test_samples_at_different_rollout_positions():
             assert_g2(np64(out), want, f"sample {b} chunk {j}", max_norm=_max_gate(n_k))
             ring.commit()
     assert rings[0].committed == 6 and rings[1].committed == 3
+
+
+def test_checkpoint_and_resume_is_exact():
+    """Seven chunk steps straight against three steps, a checkpoint of the ring
+    state and the cache bytes, a fresh ring and cache restored from it, and four
+    more steps: every output and the final cache agree bit for bit (the
+    long-rollout cache of the VideoMLA arXiv abstract, resumed mid-rollout)."""
+    mla = need_gpu()
+    dims = mla.Dims(batch=1)
+    rng = np.random.default_rng(21)
+    D, H, dh, dc, dr = 1536, 12, 128, 192, 32
+    w_dkv = _bf16(rng.standard_normal((dc, D), np.float32) / np.sqrt(D)).cuda()
+    w_kr = _bf16(rng.standard_normal((dr, D), np.float32) / np.sqrt(D)).cuda()
+    w_uk = _bf16(rng.standard_normal((H, dh, dc), np.float32) / np.sqrt(dc)).cuda()
+    w_uv = _bf16(rng.standard_normal((H, dh, dc), np.float32) / np.sqrt(dc)).cuda()
+    scale = 1.0 / np.sqrt(dh + dr)
+    steps = []
+    for j in range(CHUNKS):
+        pos = torch.from_numpy(synth.chunk_positions(range(FRAMES_PER_CHUNK * j, FRAMES_PER_CHUNK * (j + 1)), GRID))
+        steps.append(tuple(t.cuda() for t in (_bf16(rng.standard_normal((1, C, D), np.float32)),
+                                              _bf16(rng.standard_normal((1, C, H, dh), np.float32)),
+                                              _bf16(rng.standard_normal((1, C, H, dr), np.float32)), pos)))
+
+    def run(ring, cache, chunks):
+        outs = []
+        for j in chunks:
+            x, q, q_r, pos = steps[j]
+            off, n_k = ring.current()
+            mla.cache_append(dims, x, w_dkv, w_kr, pos, cache, off)
+            outs.append(mla.chunk_attend(dims, q, q_r, pos, w_uk, w_uv, cache, n_k, scale))
+            ring.commit()
+        torch.cuda.synchronize()
+        return outs
+
+    ring = mla.Ring(C, SINK, WINDOW)
+    cache = torch.zeros((1, ring.capacity, dc + dr), dtype=torch.bfloat16, device="cuda")
+    straight = run(ring, cache, range(CHUNKS))
+
+    ring_a = mla.Ring(C, SINK, WINDOW)
+    cache_a = torch.zeros_like(cache)
+    first = run(ring_a, cache_a, range(3))
+    saved_state, saved_bytes = ring_a.state(), cache_a.cpu().view(torch.int16).clone()
+    del ring_a, cache_a
+    ring_b = mla.Ring.from_state(saved_state)
+    cache_b = saved_bytes.view(torch.bfloat16).cuda()
+    rest = run(ring_b, cache_b, range(3, CHUNKS))
+    for j, (a, b) in enumerate(zip(straight, first + rest)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"chunk {j}"
+    assert torch.equal(cache.view(torch.int16), cache_b.view(torch.int16))
+    assert ring_b.state() == ring.state()

@@ -81,3 +81,17 @@ def test_cache_bytes_match_the_pages_footprint():
     assert dense == 2 * 86400 * 3072 * 2
     assert round(1 - lat / dense, 3) == 0.927
     assert mla.cache_bytes(d, torch.float32, 10) == 2 * 10 * 224 * 4
+
+
+@pytest.mark.parametrize("stop", [0, 1, 3, 9])
+def test_ring_state_round_trip(stop):
+    """A ring rebuilt from a saved state hands out the same slots and key
+    counts as the original from that point on (checkpoint and resume)."""
+    a = mla.Ring(7, 1, 3)
+    for _ in range(stop):
+        a.commit()
+    b = mla.Ring.from_state(a.state())
+    for _ in range(12):
+        assert a.current() == b.current() and a.slot_chunks() == b.slot_chunks() and a.state() == b.state()
+        a.commit()
+        b.commit()
