@@ -7,8 +7,11 @@ current chunk (latent down-projection + rotated positional key), query
 absorption, the fused latent attention over every cached chunk plus the
 current one, and the merge + W_UV up-projection.  Inputs are resident in HBM
 before the timed region.  Timing uses HIP events on the stream the library
-launches on (torch's current stream); per-kernel durations are events around
-each call inside the timed steps.
+launches on (torch's current stream): one pair around the K timed steps, with
+nothing recorded between kernels; per-kernel durations come from a second pass
+of K steps with events around each call.  The line names the library it
+measured (path and sha256; an MLA_HIP_LIB override is refused) and the host
+CPU the oracle baseline ran on.
 
 Prints one JSON line.  `value` is algorithmic TFLOP/s of the step (absorbed
 count: B*Nq*H*[Nk*(4 d_c + 2 d_r) + 4 d_h d_c] plus the append's
@@ -70,15 +73,39 @@ def load_traffic(workload: str, d_c: int):
     return t.get("hbm_bytes_per_launch")
 
 
+def host_cpu() -> dict:
+    """CPU model, the cores this process may run on, and the BLAS thread count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = None
+    return {"model": model, "cores": len(os.sched_getaffinity(0)), "blas_threads": blas}
+
+
+def library_identity(path: str) -> dict:
+    h = hashlib.sha256()
+    with open(path, "rb") as f:
+        for block in iter(lambda: f.read(1 << 20), b""):
+            h.update(block)
+    return {"path": os.path.relpath(path, ROOT), "sha256": h.hexdigest()}
+
+
 def cpu_baseline(wl, inputs, n_heads: int) -> dict:
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload:
     every query row of the first `n_heads` heads of sample 0, against all keys."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    host = host_cpu()
+    threads = host["blas_threads"] or host["cores"]
     hh, ii = np.meshgrid(np.arange(min(n_heads, wl.n_heads)), np.arange(wl.n_q), indexing="ij")
     rows = np.stack([np.zeros(hh.size, np.int64), ii.ravel(), hh.ravel()], 1)   # batch 0
     args = [inputs[k].cpu().double().numpy() for k in ("q", "q_r")]
@@ -98,6 +125,7 @@ def cpu_baseline(wl, inputs, n_heads: int) -> dict:
     dt = time.perf_counter() - t0
     flops = float(kv.sum()) * (4 * wl.d_c + 2 * wl.d_r) + len(rows) * 4 * wl.head_dim * wl.d_c
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": host["model"], "cores_available": host["cores"], "blas_threads": host["blas_threads"],
             "sample": f"{len(rows)} rows (all {wl.n_q} queries of heads 0..{min(n_heads, wl.n_heads) - 1}, "
                       f"batch 0) against their visible keys (of {wl.n_k}), fp64 "
                       f"non-absorbed numpy oracle incl. per-head K/V reconstruction; {dt:.1f} s wall; "
@@ -178,6 +206,10 @@ def main(argv=None) -> int:
                                    "(the path would shard by batch or query rows over a replicated latent cache)", "n_gpus": args.gpus}))
         return 2
 
+    if os.environ.get("MLA_HIP_LIB"):
+        print(json.dumps({"error": "MLA_HIP_LIB is set: the benchmark measures only the in-tree "
+                                   "latent_kv_cache_chunk_amd/libmla_hip.so"}))
+        return 2
     import torch
     from latent_kv_cache_chunk_amd import mla, synth
 
@@ -226,17 +258,25 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         print(json.dumps({"traffic_probe": True, "copy_bytes": COPY_BYTES, "steps": 3, "workload": wl.name}))
         return 0
+    # The timed region holds the K steps and nothing else: an event recorded
+    # between two kernels adds a few microseconds of its own, so the per-kernel
+    # breakdown comes from a second pass of K steps with events around each call.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+    if flush is None:
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(args.steps):
+            step()
+        stop.record()
+        torch.cuda.synchronize()
     torch.cuda.synchronize()
-    start.record()
     for i in range(args.steps):
         if flush is not None:
             flush.fill_(i & 0xFF)   # evicts the latent cache and q from L2 and the 256 MB last-level cache
         step(evs[i])
-    stop.record()
     torch.cuda.synchronize()
     per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])   # [steps, 4]
     ms_step = start.elapsed_time(stop) / args.steps if flush is None else float(np.mean(per.sum(axis=1)))
@@ -313,6 +353,7 @@ def main(argv=None) -> int:
                                  f"{wl.batch * wl.n_heads * wl.visible_keys()} visible pairs per launch "
                                  f"({wl.batch * wl.n_q * wl.n_heads} rows, {wl.n_k} keys)"},
         "cpu_baseline": None,
+        "library": library_identity(mla.LIB_PATH),
     }
     if not args.no_compare and not wl.causal:
         res["comparison"] = compare(wl, dims, t, absorb_ms + attend_ms + upproj_ms, args.seed, dev)
