@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace mla {
 
 typedef uint16_t u16;
@@ -156,7 +158,11 @@ inline Plan make_plan(int B, int H, int n_q, int n_k, int d_c, int d_r, bool f32
     if (G > p.U) G = p.U;
     if (G > (int64_t)p.nrb * kMaxSplitsPerBlock) G = (int64_t)p.nrb * kMaxSplitsPerBlock;
   }
-  const int64_t g_slots = G > kPartitionCUs ? G : kPartitionCUs;   // covers the chunk-causal G too
+  // Slots for the workgroups' partial states: enough for this G and for the G
+  // of any chunk-causal call of the same sizes (at most min(kPartitionCUs,
+  // nrb * kMaxSplitsPerBlock)), so the workspace size does not depend on `vis`.
+  const int64_t causal_g = std::min<int64_t>(kPartitionCUs, (int64_t)p.nrb * kMaxSplitsPerBlock);
+  const int64_t g_slots = G > causal_g ? G : causal_g;
   if (!f32 && vis != nullptr && vis->chunk_len != 0) {
     int64_t per_b = 0;
     for (int rbl = 0; rbl < p.rb_per_b; ++rbl)
