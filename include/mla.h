@@ -137,6 +137,24 @@ int32_t mla_chunk_attend(const mla_dims* dims, int32_t in_dtype, int32_t out_dty
                          float softmax_scale, void* out,
                          void* workspace, int64_t workspace_bytes, void* stream);
 
+/* mla_chunk_attend without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and validation
+ * as mla_chunk_attend, minus the workspace: the library's own static device
+ * array of MLA_NOALLOC_SCRATCH_BYTES per GPU serves instead (held from the
+ * first call on a device until the process ends).  Sizes whose workspace
+ * (mla_chunk_attend_workspace_bytes) exceeds it return MLA_ERR_WORKSPACE,
+ * before anything is enqueued.  Allocates nothing, on the host or the device.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or threads without ordering) race and must be
+ * serialized by the caller. */
+#define MLA_NOALLOC_SCRATCH_BYTES (128ll << 20)
+int32_t mla_chunk_attend_noalloc(const mla_dims* dims, int32_t in_dtype, int32_t out_dtype,
+                                 const void* q, const void* q_r, const int32_t* q_pos, int32_t n_q,
+                                 const void* w_uk, const void* w_uv,
+                                 const void* cache, int32_t cache_capacity, int32_t n_k,
+                                 float softmax_scale, void* out, void* stream);
+
 /* Chunk-causal visibility for a call whose queries span several chunks (the
  * training / teacher-forcing form; VideoMLA atlas.scime.ai summary, first
  * paragraph: causal across chunks, bidirectional inside a chunk).  Query i

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "mla_common.h"
 #include "mla_kernels.h"
@@ -447,6 +448,73 @@ int32_t mla_chunk_attend_auto(const mla_dims* dims, int32_t in_dtype, int32_t ou
                                      softmax_scale, out, workspace, workspace_bytes, stream);
   return chunk_attend_impl(dims, in_dtype, out_dtype, q, q_r, q_pos, n_q, w_uk, w_uv, cache, cache_capacity, n_k,
                            nullptr, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Chunk step with the library's own scratch (callers that cannot allocate).
+//
+// The workspace of mla_chunk_attend lives in a static device array of
+// MLA_NOALLOC_SCRATCH_BYTES.  Its address on a device is taken once, with that
+// device current, and kept per device; host code never uses the array's name
+// as an address (on the host it is only a stand-in for the symbol).  Nothing
+// in the workspace needs to start at zero: every kernel writes what it reads.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int64_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream`.
+int32_t scratch_for(hipStream_t stream, void** ptr) {
+  int cur = -1, dev = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(MLA_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr)
+      return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_chunk_attend_noalloc(const mla_dims* dims, int32_t in_dtype, int32_t out_dtype, const void* q,
+                                 const void* q_r, const int32_t* q_pos, int32_t n_q, const void* w_uk,
+                                 const void* w_uv, const void* cache, int32_t cache_capacity, int32_t n_k,
+                                 float softmax_scale, void* out, void* stream) {
+  mla::Plan p;
+  int32_t st = check_attend_sizes(dims, in_dtype, n_q, n_k, &p);
+  if (st) return st;
+  if (p.total > kScratchBytes)
+    return fail(MLA_ERR_WORKSPACE, "these sizes need %lld bytes of workspace; the no-allocation entry point has %lld",
+                (long long)p.total, (long long)kScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_for((hipStream_t)stream, &ws))) return st;
+  return chunk_attend_impl(dims, in_dtype, out_dtype, q, q_r, q_pos, n_q, w_uk, w_uv, cache, cache_capacity, n_k,
+                           nullptr, softmax_scale, out, ws, kScratchBytes, stream);
 }
 
 const char* mla_status_string(int32_t status) {

@@ -32,7 +32,8 @@ EXPORTED = ("mla_cache_append", "mla_chunk_attend_workspace_bytes", "mla_chunk_a
             "mla_cache_bytes", "mla_dense_kv_bytes", "mla_ring_last_error",
             "mla_mha_attend_workspace_bytes", "mla_mha_attend",
             "mla_chunk_attend_expanded_workspace_bytes", "mla_chunk_attend_expanded",
-            "mla_chunk_attend_form", "mla_chunk_attend_auto_workspace_bytes", "mla_chunk_attend_auto")
+            "mla_chunk_attend_form", "mla_chunk_attend_auto_workspace_bytes", "mla_chunk_attend_auto",
+            "mla_chunk_attend_noalloc")
 
 
 class MlaDims(ctypes.Structure):
@@ -92,6 +93,11 @@ _lib.mla_chunk_attend_auto_workspace_bytes.argtypes = [_DIMS, _I32, _I32, _I32]
 _lib.mla_chunk_attend_auto_workspace_bytes.restype = _I64
 _lib.mla_chunk_attend_auto.argtypes = list(_lib.mla_chunk_attend.argtypes)
 _lib.mla_chunk_attend_auto.restype = _I32
+
+_lib.mla_chunk_attend_noalloc.argtypes = [_DIMS, _I32, _I32, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, ctypes.c_float,
+                                          _P, _P]
+_lib.mla_chunk_attend_noalloc.restype = _I32
+NOALLOC_SCRATCH_BYTES = 128 << 20     # MLA_NOALLOC_SCRATCH_BYTES in mla.h
 
 _lib.mla_ring_init.argtypes = [_RING, _I32, _I32, _I32]
 _lib.mla_ring_init.restype = _I32
@@ -255,6 +261,21 @@ def chunk_attend(dims: Dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k: int, scale: 
         cz = MlaCausal(int(causal[0]), int(causal[1]))
         code = _lib.mla_chunk_attend_causal(ctypes.byref(d), *args, ctypes.byref(cz), *tail)
         _raise(code, "mla_chunk_attend_causal")
+    return out
+
+
+def chunk_attend_noalloc(dims: Dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k: int, scale: float, out,
+                         stream=None) -> torch.Tensor:
+    """chunk_attend through mla_chunk_attend_noalloc: the library's static scratch
+    replaces the workspace and nothing is allocated (out is the caller's)."""
+    n_q, dt = _attend_checks(dims, q, q_r, q_pos, w_uk, w_uv, cache, n_k)
+    _check(out, "out", (dims.batch, n_q, dims.n_heads, dims.head_dim), out.dtype)
+    d = dims.c()
+    code = _lib.mla_chunk_attend_noalloc(ctypes.byref(d), _dtype_code(dt), _dtype_code(out.dtype), q.data_ptr(),
+                                         q_r.data_ptr(), q_pos.data_ptr(), n_q, w_uk.data_ptr(), w_uv.data_ptr(),
+                                         cache.data_ptr(), cache.shape[1], int(n_k), float(scale), out.data_ptr(),
+                                         _stream(stream))
+    _raise(code, "mla_chunk_attend_noalloc")
     return out
 
 
