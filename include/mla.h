@@ -36,11 +36,17 @@
  *     mla_last_error() gives a human-readable reason (thread-local).
  *   - The library keeps no global mutable state; calls are thread-safe.
  *     Calls that share a workspace must be ordered on one stream.
- *   - MLA_ATTEND_HEADROOM (read at each call; default 32, range 0..64) sets how
- *     far, in log2 units, scores may rise above a key segment's first-block
- *     maximum before that segment is redone as an exact two-pass softmax.  It
- *     changes rounding only, never the result beyond it; tests lower it to
- *     exercise the two-pass path.
+ *   - MLA_ATTEND_HEADROOM (read at each call; default 32, range 0..64) bounds
+ *     the single-pass softmax of every bf16 attention kernel.  A key segment's
+ *     reference maximum is its first 32-key block's; if, for some row, the
+ *     running sum of p = 2^(s - m) over the keys one lane holds (half of the
+ *     segment's keys) exceeds 2^headroom, or an accumulator is not finite, the
+ *     segment is redone as an exact two-pass softmax.  Since every p <= that
+ *     sum, no score then exceeds the reference maximum by more than headroom
+ *     log2 units.  The rule is conservative (many keys near the maximum also
+ *     trigger it once headroom < log2(keys per lane)); it changes rounding
+ *     only, never the result beyond it.  Tests lower it to exercise the
+ *     two-pass path.
  *   - dtype MLA_BF16 means every floating-point input of the call is bfloat16;
  *     MLA_F32 means every one is float32.  Positions are always int32.
  *

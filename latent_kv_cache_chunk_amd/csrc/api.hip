@@ -42,8 +42,10 @@ int32_t finish(hipError_t launched, hipStream_t s, const char* what) {
   return MLA_OK;
 }
 
-// Headroom (log2 units) the single-pass attention allows above a segment's
-// first-block max before it redoes the segment in two exact passes.  32 by
+// Headroom (log2 units) of the single-pass attention: a key segment whose
+// lane-wise running sum of p = 2^(s - m) exceeds 2^headroom (m = its
+// first-block max; every p is at most that sum, so no score exceeds m by more)
+// is redone in two exact passes, in every bf16 attention kernel.  32 by
 // default; MLA_ATTEND_HEADROOM (read at every call) overrides it, so tests can
 // set it small and exercise the two-pass path on ordinary inputs.
 float attend_headroom() {

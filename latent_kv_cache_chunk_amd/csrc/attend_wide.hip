@@ -27,12 +27,13 @@
 // current one is used; one barrier per tile.
 //
 // Softmax without in-loop rescaling: each row's reference max m is fixed by
-// the first 32-key block of a segment, and later scores may exceed it by up
-// to `headroom` in log2 units (32 by default): p = 2^(s - m) stays below
-// 2^headroom, far inside the fp32/bf16 range, and the result is the same
-// softmax.  If any row of a workgroup exceeded the headroom anywhere in a
-// segment (checked once, at its end), the segment is redone exactly: a
-// max-only sweep, then accumulation against the true max.
+// the first 32-key block of a segment and p = 2^(s - m) is accumulated as is
+// (numerator and denominator share m, so the softmax is unchanged).  Later
+// keys may score above m.  Every p >= 0, so a lane's running sum bounds each
+// of its p: one check per segment -- a lane's sum above 2^headroom (32 by
+// default) or an accumulator that is not finite -- decides whether the
+// segment is redone exactly: a max-only sweep, then accumulation against the
+// true max.  The same rule as the role-split kernels (attend.hip).
 #include "mla_common.h"
 #include "mla_kernels.h"
 
@@ -154,14 +155,13 @@ __device__ __forceinline__ void block_scores(const WaveState<DC, QB>& st, const 
 
 // Softmax of one 32-key block: scores s (base-2 logits, masked keys = -inf)
 // -> bf16 P operands.  kMax only raises the reference max.  kSingle fixes the
-// reference max at the segment's first block and flags rows that exceed it by
-// more than `headroom`.
+// reference max at the segment's first block.
 template <int DC, int QB, Pass P>
 __device__ __forceinline__ void block_softmax(WaveState<DC, QB>& st, f32x16 (&s)[QB], bf16x8 (&pb)[QB][2],
-                                              bool first_block, float headroom, bool& over) {
+                                              bool first_block) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    if (P != Pass::kAccum) {
+    if (P == Pass::kMax || (P == Pass::kSingle && first_block)) {
       float mx = s[qb][0];
 #pragma unroll
       for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[qb][v]);
@@ -170,8 +170,7 @@ __device__ __forceinline__ void block_softmax(WaveState<DC, QB>& st, f32x16 (&s)
         st.m_ref[qb] = fmaxf(st.m_ref[qb], mx);
         continue;
       }
-      st.m_ref[qb] = first_block ? mx : st.m_ref[qb];
-      over |= mx > st.m_ref[qb] + headroom;
+      st.m_ref[qb] = mx;
     }
     // a row with no visible key in this segment keeps m = -inf and p = 0
     const float m = st.m_ref[qb] == -INFINITY ? 0.f : st.m_ref[qb];
@@ -220,7 +219,7 @@ __device__ __forceinline__ void block_pv(WaveState<DC, QB>& st, const char* bloc
 // the tile that exist; blocks past it are skipped, keys past it masked.
 template <int DC, int QB, int NW, Pass P>
 __device__ __forceinline__ void attend_tile(WaveState<DC, QB>& st, const char* tile, int key0, int left, int s_off,
-                                            int v_off, int half, bool first_tile, float headroom, bool& over) {
+                                            int v_off, int half, bool first_tile) {
   using L = AttendTile<DC, NW>;
   constexpr int ROWB = L::ROWB;
 #pragma unroll 1
@@ -247,7 +246,7 @@ __device__ __forceinline__ void attend_tile(WaveState<DC, QB>& st, const char* t
         for (int v = 0; v < 16; ++v)
           if ((v >> 2) * 8 + (v & 3) >= thr) s[qb][v] = -INFINITY;
     }
-    block_softmax<DC, QB, P>(st, s, pb, first_tile && kb == 0, headroom, over);
+    block_softmax<DC, QB, P>(st, s, pb, first_tile && kb == 0);
     if (P != Pass::kMax) block_pv<DC, QB, ROWB>(st, tile + kb * 32 * ROWB, v_off, pb);
   }
 }
@@ -255,14 +254,14 @@ __device__ __forceinline__ void attend_tile(WaveState<DC, QB>& st, const char* t
 // Sweep tiles [t0, t1) of one segment through the two LDS buffers (each
 // buffer a distinct LDS object, so that reads of one tile are not ordered
 // behind the in-flight direct loads of the other).  kSingle returns true,
-// identically in every wave, if some row exceeded the headroom.
+// identically in every wave, if some lane's running sum rose above
+// 2^headroom or some accumulator is not finite.
 template <int DC, int QB, int NW, Pass P>
 __device__ __forceinline__ bool sweep(WaveState<DC, QB>& st, char* sbuf0, char* sbuf1, const char* gbase, int t0,
                                       int t1, int n_k, int wave, int lane_off, int lane_row, int s_off, int v_off,
                                       int half, float headroom) {
   using L = AttendTile<DC, NW>;
   constexpr int BN = L::BN;
-  bool over = false;
   issue_tile<DC, NW>(gbase, t0 * BN, n_k, sbuf0, wave, lane_off, lane_row);
   wait_vmcnt0();
   __syncthreads();
@@ -270,16 +269,27 @@ __device__ __forceinline__ bool sweep(WaveState<DC, QB>& st, char* sbuf0, char* 
   for (int t = t0; t < t1; t += 2) {
     // tile t is in sbuf0; tile t+1 goes to sbuf1
     if (t + 1 < t1) issue_tile<DC, NW>(gbase, (t + 1) * BN, n_k, sbuf1, wave, lane_off, lane_row);
-    attend_tile<DC, QB, NW, P>(st, sbuf0, t * BN, n_k - t * BN, s_off, v_off, half, t == t0, headroom, over);
+    attend_tile<DC, QB, NW, P>(st, sbuf0, t * BN, n_k - t * BN, s_off, v_off, half, t == t0);
     wait_vmcnt0();
     __syncthreads();
     if (t + 1 >= t1) break;
     if (t + 2 < t1) issue_tile<DC, NW>(gbase, (t + 2) * BN, n_k, sbuf0, wave, lane_off, lane_row);
-    attend_tile<DC, QB, NW, P>(st, sbuf1, (t + 1) * BN, n_k - (t + 1) * BN, s_off, v_off, half, false, headroom, over);
+    attend_tile<DC, QB, NW, P>(st, sbuf1, (t + 1) * BN, n_k - (t + 1) * BN, s_off, v_off, half, false);
     wait_vmcnt0();
     __syncthreads();
   }
-  return P == Pass::kSingle ? __syncthreads_or(over) : false;
+  if (P != Pass::kSingle) return false;
+  const float lim = __builtin_amdgcn_exp2f(headroom);
+  bool over = false;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    over |= !(st.l_run[qb] <= lim);
+#pragma unroll
+    for (int cb = 0; cb < WaveState<DC, QB>::CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) over |= !(fabsf(st.oacc[qb][cb][v]) <= 3.0e38f);
+  }
+  return __syncthreads_or(over);
 }
 
 template <int DC, int QB>
@@ -365,7 +375,7 @@ void attend_wide_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstrid
     st.kv_min = kvm;
     if (te > t0 && sweep<DC, QB, NW, Pass::kSingle>(st, sbuf0, sbuf1, gbase, t0, te, n_k, wave, lane_off, lane_row,
                                                     s_off, v_off, half, headroom)) {
-      // Some score rose more than the headroom above its first-block max:
+      // A lane's running sum rose above 2^headroom (or an accumulator is not finite):
       // exact two-pass evaluation of this segment.
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) st.m_ref[qb] = -INFINITY;
