@@ -490,7 +490,7 @@ int32_t scratch_for(hipStream_t stream, void** ptr) {
       return fail(MLA_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (dev != cur) hipSetDevice(cur);
+    if (dev != cur) (void)hipSetDevice(cur);
     if (e != hipSuccess || p == nullptr)
       return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
     g_scratch_ptr[dev] = p;
