@@ -185,22 +185,36 @@ __device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile,
   using L = AttendTile<DC>;
   constexpr int KS = L::KS, PF = kScorePrefetch, NQB = ScoreState<DC>::NQB;
   const int left = c.n_k - t * L::BN;
+  // One stream of K operand reads over the tile's blocks: read g (block g /
+  // KS, k-step g % KS) goes to slot g % PF and is issued PF k-steps ahead of
+  // its MFMAs, so the next block's first reads are in flight during this
+  // block's softmax (left to itself the compiler keeps two reads in flight;
+  // the stream was 3.5% faster).  Reads of a block past the tile's last key
+  // are issued and unused.
+  bf16x8 a[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) a[i] = *reinterpret_cast<const bf16x8*>(tile + c.s_off + i * 32);
 #pragma unroll
   for (int kb = 0; kb < L::NBLK; ++kb) {
     if (kb > 0 && kb * 32 >= left) break;
-    const char* kbase = tile + kb * 32 * L::ROWB + c.s_off;
     f32x16 s[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) s[qb] = f32x16{};
-    bf16x8 a[PF];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) a[i] = *reinterpret_cast<const bf16x8*>(kbase + i * 32);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 cur = a[ks % PF];
-      if (ks + PF < KS) a[ks % PF] = *reinterpret_cast<const bf16x8*>(kbase + (ks + PF) * 32);
+      const int g = kb * KS + ks;
+      const bf16x8 cur = a[g % PF];
+      const int gn = g + PF;
+      if (gn < L::NBLK * KS)
+        a[g % PF] = *reinterpret_cast<const bf16x8*>(tile + (gn / KS) * 32 * L::ROWB + c.s_off + (gn % KS) * 32);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) s[qb] = mfma_32x32x16(cur, st.qf[qb][ks], s[qb]);
+    }
+    if (kb == 0) __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NQB, 0);
+      if (kb * KS + ks + PF < L::NBLK * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     const int key0 = t * L::BN + kb * 32;
     if (c.causal) {
@@ -265,13 +279,27 @@ __device__ __forceinline__ void value_tile(ValueState<DC>& st, const char* tile,
       const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(pb + p_slot(c.group, 0, part, c.lane));
       const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(pb + p_slot(c.group, 1, part, c.lane));
       const char* vbase = blk + part * 16 * L::ROWB;
+      bf16x8 av[L::CB];
 #pragma unroll
       for (int cb = 0; cb < L::CB; ++cb) {
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + cb * 64));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + 8 * L::ROWB + cb * 64));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        st.oacc[0][cb] = mfma_32x32x16(a, p0, st.oacc[0][cb]);
-        st.oacc[1][cb] = mfma_32x32x16(a, p1, st.oacc[1][cb]);
+        av[cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int cb = 0; cb < L::CB; ++cb) {
+        st.oacc[0][cb] = mfma_32x32x16(av[cb], p0, st.oacc[0][cb]);
+        st.oacc[1][cb] = mfma_32x32x16(av[cb], p1, st.oacc[1][cb]);
+      }
+      // Issue order: the P reads and the transposed reads of three column
+      // blocks, then two MFMAs and the reads three column blocks ahead, so
+      // that each pair of MFMAs waits on reads issued two pairs earlier (the
+      // compiler otherwise waits on every read right after issuing it).
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int cb = 0; cb < L::CB; ++cb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (cb + 3 < L::CB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
   }
@@ -284,12 +312,12 @@ __device__ __forceinline__ void value_tile(ValueState<DC>& st, const char* tile,
 // k = 0 .. n (n tiles); returns true after step n.
 template <int DC, Pass P, bool SCORE, class State>
 __device__ __forceinline__ bool sweep_step(State& st, int k, int n, int t0, char* cur, char* nxt, char* prv,
-                                           char* pb0, char* pb1, const SweepCtx& c) {
+                                           char* pbuf, const SweepCtx& c) {
   if (!SCORE && k + 1 < n) issue_tile<DC>(c, t0 + k + 1, nxt);
   if constexpr (SCORE) {
-    if (k < n) score_tile<DC, P>(st, cur, (k & 1) ? pb1 : pb0, t0 + k, k == 0, c);
+    if (k < n) score_tile<DC, P>(st, cur, pbuf + ((k & 1) ? AttendTile<DC>::PBUF : 0), t0 + k, k == 0, c);
   } else {
-    if (P != Pass::kMax && k >= 1) value_tile<DC>(st, prv, (k & 1) ? pb0 : pb1, t0 + k - 1, c);
+    if (P != Pass::kMax && k >= 1) value_tile<DC>(st, prv, pbuf + ((k & 1) ? 0 : AttendTile<DC>::PBUF), t0 + k - 1, c);
   }
   wait_vmcnt0();
   __syncthreads();
@@ -301,7 +329,7 @@ __device__ __forceinline__ bool sweep_step(State& st, int k, int n, int t0, char
 // three), so reads of one are not ordered behind the in-flight direct loads
 // of another.  Score and value wavefronts run the same steps and barriers.
 template <int DC, Pass P, bool SCORE, class State>
-__device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* k2, char* pb0, char* pb1, int t0, int t1,
+__device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* k2, char* pbuf, int t0, int t1,
                                       const SweepCtx& c) {
   const int n = t1 - t0;
   if (!SCORE) issue_tile<DC>(c, t0, k0);
@@ -309,9 +337,9 @@ __device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* k2, c
   __syncthreads();
 #pragma unroll 1
   for (int k = 0;; k += 3) {
-    if (sweep_step<DC, P, SCORE>(st, k, n, t0, k0, k1, k2, pb0, pb1, c)) break;
-    if (sweep_step<DC, P, SCORE>(st, k + 1, n, t0, k1, k2, k0, pb0, pb1, c)) break;
-    if (sweep_step<DC, P, SCORE>(st, k + 2, n, t0, k2, k0, k1, pb0, pb1, c)) break;
+    if (sweep_step<DC, P, SCORE>(st, k, n, t0, k0, k1, k2, pbuf, c)) break;
+    if (sweep_step<DC, P, SCORE>(st, k + 1, n, t0, k1, k2, k0, pbuf, c)) break;
+    if (sweep_step<DC, P, SCORE>(st, k + 2, n, t0, k2, k0, k1, pbuf, c)) break;
   }
 }
 
@@ -361,8 +389,7 @@ template <int DC>
 __device__ __forceinline__ void score_role(SweepCtx& c, SegmentIter it, const u16* __restrict__ cache,
                                            int64_t cache_bstride, const u16* __restrict__ qt, int rows_pad_b,
                                            float* __restrict__ part_ml, int64_t w, float headroom,
-                                           const Visibility& vis, char* k0, char* k1, char* k2, char* pb0,
-                                           char* pb1) {
+                                           const Visibility& vis, char* k0, char* k1, char* k2, char* pbuf) {
   using L = AttendTile<DC>;
   constexpr int NQB = ScoreState<DC>::NQB;
   ScoreState<DC> st;
@@ -381,7 +408,7 @@ __device__ __forceinline__ void score_role(SweepCtx& c, SegmentIter it, const u1
       c.kv[qb] = vis.kv_of_row(it.rbl * kRowsPerBlock + c.group * kGroupRows + half_row, c.n_k);
     }
     c.kv_min = wave_min(NQB == 2 ? min(c.kv[0], c.kv[1]) : c.kv[0]);
-    if (te > it.t0) sweep<DC, Pass::kSingle, true>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
+    if (te > it.t0) sweep<DC, Pass::kSingle, true>(st, k0, k1, k2, pbuf, it.t0, te, c);
     const float lim = __builtin_amdgcn_exp2f(headroom);
     bool over = false;
 #pragma unroll
@@ -390,10 +417,10 @@ __device__ __forceinline__ void score_role(SweepCtx& c, SegmentIter it, const u1
       // A running sum rose past 2^headroom: exact two-pass evaluation.
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) st.m_ref[qb] = -INFINITY;
-      sweep<DC, Pass::kMax, true>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
+      sweep<DC, Pass::kMax, true>(st, k0, k1, k2, pbuf, it.t0, te, c);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) st.l_run[qb] = 0.f;
-      sweep<DC, Pass::kAccum, true>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
+      sweep<DC, Pass::kAccum, true>(st, k0, k1, k2, pbuf, it.t0, te, c);
     }
     const int64_t slot = seg_slot(w, it.rb);
 #pragma unroll
@@ -411,8 +438,7 @@ __device__ __forceinline__ void score_role(SweepCtx& c, SegmentIter it, const u1
 template <int DC>
 __device__ __forceinline__ void value_role(SweepCtx& c, SegmentIter it, const u16* __restrict__ cache,
                                            int64_t cache_bstride, float* __restrict__ part_L, int64_t w,
-                                           const Visibility& vis, char* k0, char* k1, char* k2, char* pb0,
-                                           char* pb1) {
+                                           const Visibility& vis, char* k0, char* k1, char* k2, char* pbuf) {
   using L = AttendTile<DC>;
   ValueState<DC> st;
   while (it.next()) {
@@ -422,7 +448,7 @@ __device__ __forceinline__ void value_role(SweepCtx& c, SegmentIter it, const u1
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int cb = 0; cb < L::CB; ++cb) st.oacc[qb][cb] = f32x16{};
-    if (te > it.t0) sweep<DC, Pass::kSingle, false>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
+    if (te > it.t0) sweep<DC, Pass::kSingle, false>(st, k0, k1, k2, pbuf, it.t0, te, c);
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -431,12 +457,12 @@ __device__ __forceinline__ void value_role(SweepCtx& c, SegmentIter it, const u1
 #pragma unroll
         for (int v = 0; v < 16; ++v) bad |= !(fabsf(st.oacc[qb][cb][v]) <= 3.0e38f);
     if (__syncthreads_or(bad)) {
-      sweep<DC, Pass::kMax, false>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
+      sweep<DC, Pass::kMax, false>(st, k0, k1, k2, pbuf, it.t0, te, c);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int cb = 0; cb < L::CB; ++cb) st.oacc[qb][cb] = f32x16{};
-      sweep<DC, Pass::kAccum, false>(st, k0, k1, k2, pb0, pb1, it.t0, te, c);
+      sweep<DC, Pass::kAccum, false>(st, k0, k1, k2, pbuf, it.t0, te, c);
     }
     const int64_t slot = seg_slot(w, it.rb);
 #pragma unroll
@@ -469,8 +495,10 @@ void attend_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstride, in
   __shared__ __attribute__((aligned(1024))) char kbuf0[L::TILEB];
   __shared__ __attribute__((aligned(1024))) char kbuf1[L::TILEB];
   __shared__ __attribute__((aligned(1024))) char kbuf2[L::TILEB];
-  __shared__ __attribute__((aligned(1024))) char pbuf0[L::PBUF];
-  __shared__ __attribute__((aligned(1024))) char pbuf1[L::PBUF];
+  // The two P buffers are one LDS object addressed by offset: a P read through
+  // a pointer chosen between two objects would not be known to miss the key
+  // buffers, and the compiler would wait for the in-flight tile loads first.
+  __shared__ __attribute__((aligned(1024))) char pbuf[2 * L::PBUF];
 
   SweepCtx c;
   c.n_k = n_k;
@@ -503,9 +531,9 @@ void attend_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstride, in
   if (blockIdx.x == 0 && threadIdx.x == 0) *hdr = PartitionHeader{U, G, units != nullptr ? 1 : 0};
   if (scorer)
     score_role<DC>(c, it, cache, cache_bstride, qt, rows_pad_b, part_ml, w, headroom, vis, kbuf0, kbuf1, kbuf2,
-                   pbuf0, pbuf1);
+                   pbuf);
   else
-    value_role<DC>(c, it, cache, cache_bstride, part_L, w, vis, kbuf0, kbuf1, kbuf2, pbuf0, pbuf1);
+    value_role<DC>(c, it, cache, cache_bstride, part_L, w, vis, kbuf0, kbuf1, kbuf2, pbuf);
 }
 
 // fp32 variant: 8 threads per row, 32 rows per workgroup, one workgroup

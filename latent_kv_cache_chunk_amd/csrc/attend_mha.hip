@@ -147,16 +147,29 @@ template <int DQK, Pass P>
 __device__ __forceinline__ void score_tile(ScoreState<DQK>& st, const char* kbuf, char* pbuf, int t, bool first,
                                            const Ctx& c) {
   using L = Tile<DQK>;
-  constexpr int KS = L::KS;
+  constexpr int KS = L::KS, PF = 4;
+  // One stream of K operand reads over both blocks, each PF k-steps ahead of
+  // its MFMAs (read g = block g / KS, k-step g % KS, in slot g % PF).
+  bf16x8 a[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) a[i] = *reinterpret_cast<const bf16x8*>(kbuf + c.s_off + i * 32);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const char* kbase = kbuf + kb * 32 * L::K::ROWB + c.s_off;
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbase + ks * 32);
-      s[0] = mfma_32x32x16(a, st.qf[0][ks], s[0]);
-      s[1] = mfma_32x32x16(a, st.qf[1][ks], s[1]);
+      const int g = kb * KS + ks, gn = g + PF;
+      const bf16x8 cur = a[g % PF];
+      if (gn < 2 * KS)
+        a[g % PF] = *reinterpret_cast<const bf16x8*>(kbuf + (gn / KS) * 32 * L::K::ROWB + c.s_off + (gn % KS) * 32);
+      s[0] = mfma_32x32x16(cur, st.qf[0][ks], s[0]);
+      s[1] = mfma_32x32x16(cur, st.qf[1][ks], s[1]);
+    }
+    if (kb == 0) __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (kb * KS + ks + PF < 2 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     const int left = c.n_k - t * kBN - kb * 32;
     if (left < 32) {
@@ -211,13 +224,25 @@ __device__ __forceinline__ void value_tile(ValueState& st, const char* vbuf, con
       const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(pbuf + p_slot(c.group, kb, 0, part, c.lane));
       const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(pbuf + p_slot(c.group, kb, 1, part, c.lane));
       const char* vb = vbuf + (kb * 32 + part * 16) * VR + c.v_off;
+      bf16x8 av[L::CB];
 #pragma unroll
       for (int cb = 0; cb < L::CB; ++cb) {
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + cb * 64));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * VR + cb * 64));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        st.oacc[0][cb] = mfma_32x32x16(a, p0, st.oacc[0][cb]);
-        st.oacc[1][cb] = mfma_32x32x16(a, p1, st.oacc[1][cb]);
+        av[cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int cb = 0; cb < L::CB; ++cb) {
+        st.oacc[0][cb] = mfma_32x32x16(av[cb], p0, st.oacc[0][cb]);
+        st.oacc[1][cb] = mfma_32x32x16(av[cb], p1, st.oacc[1][cb]);
+      }
+      // the P reads and three column blocks' reads first, then two MFMAs and
+      // the reads three column blocks ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int cb = 0; cb < L::CB; ++cb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (cb + 3 < L::CB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
 }
