@@ -155,13 +155,16 @@ __device__ __forceinline__ void block_scores(const WaveState<DC, QB>& st, const 
 
 // Softmax of one 32-key block: scores s (base-2 logits, masked keys = -inf)
 // -> bf16 P operands.  kMax only raises the reference max.  kSingle fixes the
-// reference max at the segment's first block.
+// reference max at the segment's first block.  It also flags a block max more
+// than `headroom` above the reference: the running-sum bound at the segment's
+// end implies that flag (such a p alone exceeds 2^headroom), and it is kept
+// because the code generated without it spills the accumulators.
 template <int DC, int QB, Pass P>
 __device__ __forceinline__ void block_softmax(WaveState<DC, QB>& st, f32x16 (&s)[QB], bf16x8 (&pb)[QB][2],
-                                              bool first_block) {
+                                              bool first_block, float headroom, bool& over) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    if (P == Pass::kMax || (P == Pass::kSingle && first_block)) {
+    if (P != Pass::kAccum) {
       float mx = s[qb][0];
 #pragma unroll
       for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[qb][v]);
@@ -170,7 +173,8 @@ __device__ __forceinline__ void block_softmax(WaveState<DC, QB>& st, f32x16 (&s)
         st.m_ref[qb] = fmaxf(st.m_ref[qb], mx);
         continue;
       }
-      st.m_ref[qb] = mx;
+      st.m_ref[qb] = first_block ? mx : st.m_ref[qb];
+      over |= mx > st.m_ref[qb] + headroom;
     }
     // a row with no visible key in this segment keeps m = -inf and p = 0
     const float m = st.m_ref[qb] == -INFINITY ? 0.f : st.m_ref[qb];
@@ -201,17 +205,31 @@ template <int DC, int QB, int ROWB>
 __device__ __forceinline__ void block_pv(WaveState<DC, QB>& st, const char* block_row0, int v_off,
                                          const bf16x8 (&pb)[QB][2]) {
   constexpr int CB = WaveState<DC, QB>::CB;
+  // One stream of transposed reads over (part, column block), RA items ahead
+  // of their MFMAs (the compiler otherwise waits on each read right after
+  // issuing it).
+  constexpr int NIT = 2 * CB, RA = 3;
+  bf16x8 av[RA];
+  auto vread = [&](int it) {
+    const char* vb = block_row0 + (it / CB) * 16 * ROWB + v_off + (it % CB) * 64;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * ROWB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 #pragma unroll
-  for (int part = 0; part < 2; ++part) {
-    const char* vbase = block_row0 + part * 16 * ROWB + v_off;
+  for (int it = 0; it < RA; ++it) av[it] = vread(it);
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + cb * 64));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + 8 * ROWB + cb * 64));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  for (int it = 0; it < NIT; ++it) {
+    const bf16x8 a = av[it % RA];
+    if (it + RA < NIT) av[it % RA] = vread(it + RA);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) st.oacc[qb][cb] = mfma_32x32x16(a, pb[qb][part], st.oacc[qb][cb]);
-    }
+    for (int qb = 0; qb < QB; ++qb) st.oacc[qb][it % CB] = mfma_32x32x16(a, pb[qb][it / CB], st.oacc[qb][it % CB]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * RA, 0);
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+    if (it + RA < NIT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
 }
 
@@ -219,7 +237,7 @@ __device__ __forceinline__ void block_pv(WaveState<DC, QB>& st, const char* bloc
 // the tile that exist; blocks past it are skipped, keys past it masked.
 template <int DC, int QB, int NW, Pass P>
 __device__ __forceinline__ void attend_tile(WaveState<DC, QB>& st, const char* tile, int key0, int left, int s_off,
-                                            int v_off, int half, bool first_tile) {
+                                            int v_off, int half, bool first_tile, float headroom, bool& over) {
   using L = AttendTile<DC, NW>;
   constexpr int ROWB = L::ROWB;
 #pragma unroll 1
@@ -246,7 +264,7 @@ __device__ __forceinline__ void attend_tile(WaveState<DC, QB>& st, const char* t
         for (int v = 0; v < 16; ++v)
           if ((v >> 2) * 8 + (v & 3) >= thr) s[qb][v] = -INFINITY;
     }
-    block_softmax<DC, QB, P>(st, s, pb, first_tile && kb == 0);
+    block_softmax<DC, QB, P>(st, s, pb, first_tile && kb == 0, headroom, over);
     if (P != Pass::kMax) block_pv<DC, QB, ROWB>(st, tile + kb * 32 * ROWB, v_off, pb);
   }
 }
@@ -262,6 +280,7 @@ __device__ __forceinline__ bool sweep(WaveState<DC, QB>& st, char* sbuf0, char* 
                                       int half, float headroom) {
   using L = AttendTile<DC, NW>;
   constexpr int BN = L::BN;
+  bool over = false;
   issue_tile<DC, NW>(gbase, t0 * BN, n_k, sbuf0, wave, lane_off, lane_row);
   wait_vmcnt0();
   __syncthreads();
@@ -269,25 +288,27 @@ __device__ __forceinline__ bool sweep(WaveState<DC, QB>& st, char* sbuf0, char* 
   for (int t = t0; t < t1; t += 2) {
     // tile t is in sbuf0; tile t+1 goes to sbuf1
     if (t + 1 < t1) issue_tile<DC, NW>(gbase, (t + 1) * BN, n_k, sbuf1, wave, lane_off, lane_row);
-    attend_tile<DC, QB, NW, P>(st, sbuf0, t * BN, n_k - t * BN, s_off, v_off, half, t == t0);
+    attend_tile<DC, QB, NW, P>(st, sbuf0, t * BN, n_k - t * BN, s_off, v_off, half, t == t0, headroom, over);
     wait_vmcnt0();
     __syncthreads();
     if (t + 1 >= t1) break;
     if (t + 2 < t1) issue_tile<DC, NW>(gbase, (t + 2) * BN, n_k, sbuf0, wave, lane_off, lane_row);
-    attend_tile<DC, QB, NW, P>(st, sbuf1, (t + 1) * BN, n_k - (t + 1) * BN, s_off, v_off, half, false);
+    attend_tile<DC, QB, NW, P>(st, sbuf1, (t + 1) * BN, n_k - (t + 1) * BN, s_off, v_off, half, false, headroom, over);
     wait_vmcnt0();
     __syncthreads();
   }
   if (P != Pass::kSingle) return false;
+  // The segment's running sums (and accumulators, whose magnitudes are summed:
+  // an inf or NaN among them carries through) against the bound.
   const float lim = __builtin_amdgcn_exp2f(headroom);
-  bool over = false;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    over |= !(st.l_run[qb] <= lim);
+    float asum = 0.f;
 #pragma unroll
     for (int cb = 0; cb < WaveState<DC, QB>::CB; ++cb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) over |= !(fabsf(st.oacc[qb][cb][v]) <= 3.0e38f);
+      for (int v = 0; v < 16; ++v) asum += fabsf(st.oacc[qb][cb][v]);
+    over |= !(st.l_run[qb] <= lim) || !(asum <= 3.0e38f);
   }
   return __syncthreads_or(over);
 }
