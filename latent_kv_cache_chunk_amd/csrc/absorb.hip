@@ -38,10 +38,17 @@ void rope_table_kernel(const int* __restrict__ q_pos, int n_q, int pairs, RopeSp
 // Finished rows go through LDS (over the W_UK stage, after a barrier): a
 // wavefront's 32 rows of q~ are contiguous in memory and leave as whole
 // 16-byte pieces of consecutive addresses.
+//
+// Workgroup id -> (sample b, head h, query block y): a 128-byte line of q_r
+// holds two heads' 32 values, so the heads 2k and 2k+1 of one query block get
+// ids 8 apart -- the same XCD (workgroups are dealt to the eight XCDs round
+// robin) and neighbours in its dispatch order -- and the line is fetched into
+// one L2 once.  Units u = (b * ceil(H/2) + k) * NY + y; id = 16*(u/8) +
+// 8*(h%2) + u%8.
 template <int DC>
 __global__ __launch_bounds__(256)
 void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
-                        const f32x2* __restrict__ rope_cs, int n_q, int H,
+                        const f32x2* __restrict__ rope_cs, int n_q, int H, int B,
                         const u16* __restrict__ w_uk, float qscale,
                         u16* __restrict__ qt, int rows_pad_b) {
   constexpr int DH = 128, DR = 32, W = DC + DR, CB = DC / 32;
@@ -51,9 +58,13 @@ void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
   static_assert(((W * 2 + 16) / 16) & 1, "odd slot stride");
   constexpr int WBYTES = DH * ROWB, OBYTES = 4 * 32 * OROW;
   __shared__ __attribute__((aligned(16))) char wl[WBYTES > OBYTES ? WBYTES : OBYTES];
-  const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
+  const int ny = (n_q + 127) / 128, hp = (H + 1) / 2;
+  const int u = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
+  const int y = u % ny, bk = u / ny, b = bk / hp;
+  const int h = 2 * (bk - b * hp) + ((blockIdx.x >> 3) & 1);
+  if (b >= B || h >= H) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
-  const int i0 = blockIdx.y * 128 + wave * 32;           // first query of this wavefront
+  const int i0 = y * 128 + wave * 32;                    // first query of this wavefront
   const int i = i0 + (lane & 31);
   const bool ok = i < n_q;
 
@@ -139,7 +150,7 @@ void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
 
   // Padding rows after the last real row of each sample are zero so that the
   // attention kernel reads only finite values.
-  if (h == 0 && blockIdx.y == 0) {
+  if (h == 0 && y == 0) {
     const int rows_b = H * n_q;
     u16* pad = qt + ((int64_t)b * rows_pad_b + rows_b) * W;
     const int64_t n = (int64_t)(rows_pad_b - rows_b) * W / 8;
@@ -195,16 +206,17 @@ hipError_t launch_absorb_bf16(const Plan& p, const AbsorbArgs& a, hipStream_t s)
   f32x2* cs = (f32x2*)a.rope_cs;
   rope_table_kernel<<<dim3((unsigned)((p.n_q * pairs + 255) / 256)), dim3(256), 0, s>>>(a.q_pos, p.n_q, pairs, a.rope,
                                                                                          cs);
-  const dim3 grid(p.B * p.H, (p.n_q + 127) / 128), block(256);
+  const int64_t units = (int64_t)p.B * ((p.H + 1) / 2) * ((p.n_q + 127) / 128);
+  const dim3 grid((unsigned)((units + 7) / 8 * 16)), block(256);   // see the id mapping in the kernel
   const u16* q = (const u16*)a.q;
   const u16* qr = (const u16*)a.q_r;
   const u16* wk = (const u16*)a.w_uk;
   u16* qt = (u16*)a.qt;
   switch (p.d_c) {
-    case 64: absorb_bf16_kernel<64><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, wk, a.qscale, qt, p.rows_pad_b); break;
-    case 128: absorb_bf16_kernel<128><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, wk, a.qscale, qt, p.rows_pad_b); break;
-    case 192: absorb_bf16_kernel<192><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, wk, a.qscale, qt, p.rows_pad_b); break;
-    case 256: absorb_bf16_kernel<256><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, wk, a.qscale, qt, p.rows_pad_b); break;
+    case 64: absorb_bf16_kernel<64><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, p.B, wk, a.qscale, qt, p.rows_pad_b); break;
+    case 128: absorb_bf16_kernel<128><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, p.B, wk, a.qscale, qt, p.rows_pad_b); break;
+    case 192: absorb_bf16_kernel<192><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, p.B, wk, a.qscale, qt, p.rows_pad_b); break;
+    case 256: absorb_bf16_kernel<256><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, p.B, wk, a.qscale, qt, p.rows_pad_b); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
