@@ -5,7 +5,12 @@
         <write_counter_collection.csv> --workload wan480p --command-fetch C1 --command-write C2
         --out-json profiles/attend_traffic_wan480p.json --out-md F.md
 
-`trace` turns the kernel statistics table into markdown.  `traffic` converts
+    python -m latent_kv_cache_chunk_amd.profile_summary sq <pass1_counter_collection.csv> [<pass2...>]
+        --workload wan480p --duration-us D --command C1 [--command C2] --out F.md
+
+`trace` turns the kernel statistics table into markdown.  `sq` averages the
+SQ/GRBM counters of the attention kernel over its dispatches and derives the
+matrix-core busy fraction and the shader clock.  `traffic` converts
 FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel into bytes,
 scaled by what the same counters read for the probe's calibration kernel (an
 elementwise negation that reads and writes a known number of bytes once),
@@ -73,6 +78,55 @@ def _pick(per, pattern: str):
     return hits[0]
 
 
+# MI355X: 256 compute units in 8 XCDs, 4 SIMDs (one matrix core each) per CU.
+CUS, XCDS, SIMDS_PER_CU = 256, 8, 4
+
+
+def cmd_sq(a) -> None:
+    sys.path.insert(0, ROOT)
+    import bench
+    from latent_kv_cache_chunk_amd import synth
+    d_c = synth.WORKLOADS[a.workload].d_c
+    pattern = r"mla::(wide::)?" + bench.attend_kernel(d_c)
+    means, name, n_disp = {}, None, 0
+    for path in a.passes:
+        per = defaultdict(lambda: defaultdict(list))
+        for r in csv.DictReader(open(path)):
+            per[r["Counter_Name"]][r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        for counter, kernels in per.items():
+            name, vals = _pick(kernels, pattern)
+            means[counter] = sum(vals) / len(vals)
+            n_disp = len(vals)
+    lines = [f"# SQ counters: {short_name(name)}, workload {a.workload}", "",
+             "Commands (repo root, one MI355X; one counter set per pass):", ""]
+    lines += [f"    {c}" for c in a.command]
+    lines += ["", f"Means over the {n_disp} attention dispatches of a pass; kernel duration {a.duration_us:.1f} us "
+              "(kernel trace of the same sources).", "",
+              "| Counter | Value per dispatch |", "|---|---|"]
+    lines += [f"| {k} | {v:.4g} |" for k, v in sorted(means.items())]
+    derived = []
+    if "GRBM_GUI_ACTIVE" in means:
+        cyc = means["GRBM_GUI_ACTIVE"] / XCDS
+        derived.append(f"* Shader clock: GRBM_GUI_ACTIVE / {XCDS} XCDs = {cyc:.4g} cycles per XCD over "
+                       f"{a.duration_us:.1f} us = **{cyc / a.duration_us / 1e3:.2f} GHz**.")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in means:
+            busy = means["SQ_VALU_MFMA_BUSY_CYCLES"] / (CUS * SIMDS_PER_CU * cyc)
+            derived.append(f"* Matrix cores busy: SQ_VALU_MFMA_BUSY_CYCLES / ({CUS * SIMDS_PER_CU} SIMDs x "
+                           f"{cyc:.4g} cycles) = **{100 * busy:.1f}%** of the launch.")
+    if "SQ_WAVE_CYCLES" in means and "SQ_WAIT_INST_ANY" in means:
+        derived.append(f"* Waves waiting on a dependency: SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES = "
+                       f"{100 * means['SQ_WAIT_INST_ANY'] / means['SQ_WAVE_CYCLES']:.1f}%.")
+    if "SQ_INSTS_LDS" in means and "SQ_LDS_BANK_CONFLICT" in means:
+        derived.append(f"* LDS bank-conflict cycles per LDS instruction: "
+                       f"{means['SQ_LDS_BANK_CONFLICT'] / means['SQ_INSTS_LDS']:.2f}.")
+    if derived:
+        lines += ["", "Derived:", ""] + derived
+    if a.note:
+        lines += ["", a.note]
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cmd_traffic(a) -> None:
     sys.path.insert(0, ROOT)
     import bench
@@ -138,8 +192,15 @@ def main(argv=None) -> int:
     f.add_argument("--note", default="")
     f.add_argument("--out-json", required=True)
     f.add_argument("--out-md", required=True)
+    q = sub.add_parser("sq")
+    q.add_argument("passes", nargs="+")
+    q.add_argument("--workload", default="wan480p")
+    q.add_argument("--duration-us", type=float, required=True)
+    q.add_argument("--command", action="append", required=True)
+    q.add_argument("--note", default="")
+    q.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    {"trace": cmd_trace, "traffic": cmd_traffic}[a.cmd](a)
+    {"trace": cmd_trace, "traffic": cmd_traffic, "sq": cmd_sq}[a.cmd](a)
     return 0
 
 
