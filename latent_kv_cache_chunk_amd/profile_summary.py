@@ -9,8 +9,8 @@
         --workload wan480p --duration-us D --command C1 [--command C2] --out F.md
 
 `trace` turns the kernel statistics table into markdown.  `sq` averages the
-SQ/GRBM counters of the attention kernel over its dispatches and derives the
-matrix-core busy fraction and the shader clock.  `traffic` converts
+SQ/GRBM counters of the attention kernel over its dispatches (warmup dropped)
+and derives the matrix-core busy fraction and the shader clock per dispatch.  `traffic` converts
 FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel into bytes,
 scaled by what the same counters read for the probe's calibration kernel (an
 elementwise negation that reads and writes a known number of bytes once),
@@ -83,36 +83,57 @@ CUS, XCDS, SIMDS_PER_CU = 256, 8, 4
 
 
 def cmd_sq(a) -> None:
+    """SQ/GRBM counters of the attention kernel, per dispatch.  The first
+    `skip` dispatches of a pass are dropped: the first one's GRBM_GUI_ACTIVE
+    also counts cycles outside the kernel (it implies more than the part's
+    2.4 GHz).  The clock of a dispatch is its GRBM_GUI_ACTIVE per XCD over its
+    own duration in the same run (the counter runs are slower than unprofiled
+    ones; the ratio is what the counters measure)."""
     sys.path.insert(0, ROOT)
     import bench
     from latent_kv_cache_chunk_amd import synth
     d_c = synth.WORKLOADS[a.workload].d_c
     pattern = r"mla::(wide::)?" + bench.attend_kernel(d_c)
-    means, name, n_disp = {}, None, 0
+    name, means, clocks, busys, durs, n_kept = None, {}, [], [], [], 0
     for path in a.passes:
-        per = defaultdict(lambda: defaultdict(list))
+        disp = defaultdict(dict)
         for r in csv.DictReader(open(path)):
-            per[r["Counter_Name"]][r["Kernel_Name"]].append(float(r["Counter_Value"]))
-        for counter, kernels in per.items():
-            name, vals = _pick(kernels, pattern)
-            means[counter] = sum(vals) / len(vals)
-            n_disp = len(vals)
+            if not re.search(pattern, r["Kernel_Name"]):
+                continue
+            name = r["Kernel_Name"]
+            d = disp[int(r["Dispatch_Id"])]
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+            d["_dur_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        kept = [disp[k] for k in sorted(disp)][a.skip:]
+        if not kept:
+            raise SystemExit(f"no dispatch of {pattern!r} left in {path}")
+        n_kept = len(kept)
+        for c in kept[0]:
+            if c != "_dur_us":
+                means[c] = sum(d[c] for d in kept) / len(kept)
+        for d in kept:
+            if "GRBM_GUI_ACTIVE" in d:
+                cyc = d["GRBM_GUI_ACTIVE"] / XCDS
+                clocks.append(cyc / d["_dur_us"] / 1e3)
+                durs.append(d["_dur_us"])
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in d:
+                    busys.append(d["SQ_VALU_MFMA_BUSY_CYCLES"] / (CUS * SIMDS_PER_CU * cyc))
     lines = [f"# SQ counters: {short_name(name)}, workload {a.workload}", "",
              "Commands (repo root, one MI355X; one counter set per pass):", ""]
     lines += [f"    {c}" for c in a.command]
-    lines += ["", f"Means over the {n_disp} attention dispatches of a pass; kernel duration {a.duration_us:.1f} us "
-              "(kernel trace of the same sources).", "",
+    lines += ["", f"Means over {n_kept} attention dispatches of a pass (the first {a.skip} dropped: warmup). "
+              f"Unprofiled, the kernel takes {a.duration_us:.1f} us (kernel trace of the same sources); under "
+              "the counters its dispatches ran " + (f"{min(durs):.1f}-{max(durs):.1f} us." if durs else "-"), "",
               "| Counter | Value per dispatch |", "|---|---|"]
     lines += [f"| {k} | {v:.4g} |" for k, v in sorted(means.items())]
+    rng = lambda v, f: f(v[0]) if f(min(v)) == f(max(v)) else f"{f(min(v))}-{f(max(v))}"
     derived = []
-    if "GRBM_GUI_ACTIVE" in means:
-        cyc = means["GRBM_GUI_ACTIVE"] / XCDS
-        derived.append(f"* Shader clock: GRBM_GUI_ACTIVE / {XCDS} XCDs = {cyc:.4g} cycles per XCD over "
-                       f"{a.duration_us:.1f} us = **{cyc / a.duration_us / 1e3:.2f} GHz**.")
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in means:
-            busy = means["SQ_VALU_MFMA_BUSY_CYCLES"] / (CUS * SIMDS_PER_CU * cyc)
-            derived.append(f"* Matrix cores busy: SQ_VALU_MFMA_BUSY_CYCLES / ({CUS * SIMDS_PER_CU} SIMDs x "
-                           f"{cyc:.4g} cycles) = **{100 * busy:.1f}%** of the launch.")
+    if clocks:
+        derived.append(f"* Shader clock: GRBM_GUI_ACTIVE / {XCDS} XCDs over each dispatch's duration = "
+                       f"**{rng(clocks, lambda x: f'{x:.2f}')} GHz**.")
+    if busys:
+        derived.append(f"* Matrix cores busy: SQ_VALU_MFMA_BUSY_CYCLES / ({CUS * SIMDS_PER_CU} SIMDs x "
+                       f"GRBM_GUI_ACTIVE / {XCDS}) = **{rng(busys, lambda x: f'{100 * x:.1f}')}%** of the launch.")
     if "SQ_WAVE_CYCLES" in means and "SQ_WAIT_INST_ANY" in means:
         derived.append(f"* Waves waiting on a dependency: SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES = "
                        f"{100 * means['SQ_WAIT_INST_ANY'] / means['SQ_WAVE_CYCLES']:.1f}%.")
@@ -195,7 +216,8 @@ def main(argv=None) -> int:
     q = sub.add_parser("sq")
     q.add_argument("passes", nargs="+")
     q.add_argument("--workload", default="wan480p")
-    q.add_argument("--duration-us", type=float, required=True)
+    q.add_argument("--duration-us", type=float, required=True, help="unprofiled kernel time, for reference")
+    q.add_argument("--skip", type=int, default=1)
     q.add_argument("--command", action="append", required=True)
     q.add_argument("--note", default="")
     q.add_argument("--out", required=True)
