@@ -11,6 +11,20 @@
 
 namespace mla {
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Slot permutation of a staged W_UV row (NP 16-byte pieces).  With 16 lanes
+// reading one piece of 16 consecutive rows: a 128-byte row offset mod 256
+// (NP = 8, 24) puts even and odd rows in opposite bank halves, so eight
+// distinct values for each pair of rows suffice; a row stride that is a
+// multiple of 256 bytes (NP = 16, 32) needs sixteen.
+template <int NP>
+__device__ inline int wuv_swizzle(int row) {
+  static_assert(NP % 8 == 0, "whole groups of eight pieces");
+  if constexpr ((NP * 16) % 256 == 0) return row & 15;
+  else return (row >> 1) & 7;
+}
+
 // Two wavefronts per SIMD for d_c <= 192 (the merge is latency-bound); d_c =
 // 256 needs the full register file for its 128 merged channels per lane.
 template <int DC, bool OUT_F32>
@@ -26,21 +40,6 @@ void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restric
   const bool ok = i < n_q;
   const bool active = blockIdx.y * 128 + wave * 32 < n_q;   // some real row in this wavefront
 
-  // W_UV[h] (DH rows of DC bf16) staged once per workgroup; rows padded to an
-  // odd number of 16-byte slots so that the b128 operand reads are
-  // conflict-free.
-  constexpr int WROW = DC * 2 + 16;
-  __shared__ __attribute__((aligned(16))) char wsh[DH * WROW];
-  {
-    const u16* wsrc = w_uv + (int64_t)h * DH * DC;
-    constexpr int CH = DC / 8;   // 16-byte pieces per row
-    for (int q = threadIdx.x; q < DH * CH; q += 256) {
-      const int row = q / CH, ch = q - row * CH;
-      *reinterpret_cast<uint4*>(wsh + row * WROW + ch * 16) =
-          *reinterpret_cast<const uint4*>(wsrc + (int64_t)row * DC + ch * 8);
-    }
-  }
-
   const int r = h * n_q + (ok ? i : 0);
   const int64_t rb = (int64_t)b * rb_per_b + r / kRowsPerBlock;
   const int rl = r % kRowsPerBlock;
@@ -52,6 +51,29 @@ void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restric
   const int64_t* units = ph.per_block_units ? units_ws : nullptr;
   const int64_t u_first = rb_first_unit(units, T, rb), u_last = rb_first_unit(units, T, rb + 1) - 1;
   const int64_t wa = unit_owner(u_first, U, G), wb = unit_owner(u_last, U, G);
+
+  // W_UV[h] (DH rows of DC bf16) staged once per workgroup by direct-to-LDS
+  // loads, issued after the partition lookups (whose waits would otherwise
+  // wait for them too) and before the partial states, so that they land
+  // while those load.
+  // Rows are not padded (a direct load fills 64 consecutive 16-byte slots);
+  // 16-byte piece p of row r sits in slot p ^ wuv_swizzle(r) of its row, which
+  // keeps the b128 operand reads (16 lanes = 16 consecutive rows, one piece)
+  // on distinct banks.
+  constexpr int NP = DC / 8;                      // 16-byte pieces per row
+  constexpr int WROW = DC * 2;
+  __shared__ __attribute__((aligned(16))) char wsh[DH * WROW];
+  {
+    const char* wsrc = reinterpret_cast<const char*>(w_uv + (int64_t)h * DH * DC);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int k = 0; k < DH * NP / 256; ++k) {    // 64-slot loads of this wavefront
+      const int slot0 = (wave_u + 4 * k) * 64;
+      const int slot = slot0 + lane, row = slot / NP, pp = slot - row * NP;
+      const int piece = pp ^ wuv_swizzle<NP>(row);
+      __builtin_amdgcn_global_load_lds(wsrc + (row * NP + piece) * 16, (lds_void*)(wsh + slot0 * 16), 16, 0, 0);
+    }
+  }
 
   // L of this lane's row and columns {ks*16 + half*8 + e}, merged over the
   // segments in one pass with a running max M: what is summed so far is
@@ -87,6 +109,7 @@ void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restric
     }
   }
   const float inv_l = 1.f / lsum;
+  __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0): this wavefront's W_UV loads have landed
   __syncthreads();         // W_UV staged
   if (!active) return;     // no barriers follow
 
@@ -106,7 +129,8 @@ void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restric
     }
 #pragma unroll
     for (int db = 0; db < DH / 32; ++db) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(wsh + (db * 32 + (lane & 31)) * WROW + c0 * 2);
+      const int wr = db * 32 + (lane & 31);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(wsh + wr * WROW + ((c0 / 8) ^ wuv_swizzle<NP>(wr)) * 16);
       acc[db] = mfma_32x32x16(a, hi, acc[db]);
       acc[db] = mfma_32x32x16(a, lo, acc[db]);
     }
