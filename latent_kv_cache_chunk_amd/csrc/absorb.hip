@@ -68,19 +68,32 @@ void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
   const int i = i0 + (lane & 31);
   const bool ok = i < n_q;
 
+  // A thread's pieces of W_UK[h] and its q row are all loaded before the first
+  // LDS store, so the staging costs one round trip, not one per piece.
+  constexpr int PER = DH * NCH / 256;                    // 16-byte pieces per thread
+  static_assert(DH * NCH % 256 == 0, "whole pieces per thread");
   const u16* wk = w_uk + (int64_t)h * DH * DC;
-  for (int idx = threadIdx.x; idx < DH * NCH; idx += 256) {
-    const int r = idx / NCH, ch = idx - r * NCH;
-    const int rs = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-    *reinterpret_cast<uint4*>(wl + rs * ROWB + ch * 16) = *reinterpret_cast<const uint4*>(wk + r * DC + ch * 8);
+  uint4 wv[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = threadIdx.x + 256 * k, r = idx / NCH, ch = idx - r * NCH;
+    wv[k] = *reinterpret_cast<const uint4*>(wk + r * DC + ch * 8);
   }
-
   const int64_t qrow_off = (((int64_t)b * n_q + (ok ? i : 0)) * H + h);
   const u16* qrow = q + qrow_off * DH + half * 8;
   bf16x8 qf[DH / 16];
 #pragma unroll
   for (int ks = 0; ks < DH / 16; ++ks)
     qf[ks] = ok ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16) : bf16x8{};
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = threadIdx.x + 256 * k, r = idx / NCH, ch = idx - r * NCH;
+    const int rs = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+    *reinterpret_cast<uint4*>(wl + rs * ROWB + ch * 16) = wv[k];
+  }
+  // pin that order (the scheduler otherwise pairs each load with its store)
+  __builtin_amdgcn_sched_group_barrier(0x020, PER + DH / 16, 0);
+  __builtin_amdgcn_sched_group_barrier(0x200, PER, 0);
   __syncthreads();
 
   const int g = lane >> 4, j = lane & 15;
