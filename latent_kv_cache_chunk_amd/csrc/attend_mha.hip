@@ -547,9 +547,24 @@ void mha_uplift_kernel(const u16* __restrict__ cache, int64_t cap, int n_k, int 
   const bool is_v = blockIdx.z != 0;
   const int drow = is_v ? DH : DQK;    // elements per output row
   const u16* wsrc = (is_v ? w_uv : w_uk) + (int64_t)h * DH * DC;
-  for (int idx = threadIdx.x; idx < DH * CPR; idx += 512) {
-    const int r = idx / CPR, ch = idx - r * CPR;
-    *reinterpret_cast<uint4*>(wt + r * WROW + ch * 16) = *reinterpret_cast<const uint4*>(wsrc + r * DC + ch * 8);
+  {
+    // every piece of a thread is loaded before the first LDS store (one round
+    // trip, not one per piece; the scheduler would otherwise pair them)
+    constexpr int PER = DH * CPR / 512;
+    static_assert(DH * CPR % 512 == 0, "whole pieces per thread");
+    uint4 wv[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = threadIdx.x + 512 * k, r = idx / CPR, ch = idx - r * CPR;
+      wv[k] = *reinterpret_cast<const uint4*>(wsrc + r * DC + ch * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = threadIdx.x + 512 * k, r = idx / CPR, ch = idx - r * CPR;
+      *reinterpret_cast<uint4*>(wt + r * WROW + ch * 16) = wv[k];
+    }
+    __builtin_amdgcn_sched_group_barrier(0x020, PER, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, PER, 0);
   }
   u16* out = is_v ? V : K;
   char* st = stage[wave];
@@ -559,16 +574,30 @@ void mha_uplift_kernel(const u16* __restrict__ cache, int64_t cap, int n_k, int 
   // 256-token blocks blockIdx.x, blockIdx.x + gridDim.x, ...: the weight
   // stage is loaded once per workgroup, and the wavefronts run their blocks
   // without further barriers (each uses only its own staging area).
+  // Latent row of this lane's token in block tb (tokens past the last re-read
+  // it; their outputs are not stored).
+  auto cache_row = [&](int tb) {
+    const int my_tok = min(tb * 256 + wave * 32 + (lane & 31), ntok - 1);
+    const int b = my_tok / n_k, j = my_tok - b * n_k;
+    return cache + ((int64_t)b * cap + j) * W;
+  };
+  // The next block's latent rows load while this block computes.
+  bf16x8 cf[KS];
+  {
+    const u16* crow = cache_row(blockIdx.x);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) cf[k] = *reinterpret_cast<const bf16x8*>(crow + k * 16 + half * 8);
+  }
 #pragma unroll 1
   for (int tb = blockIdx.x; tb * 256 < ntok; tb += gridDim.x) {
     const int tok0 = tb * 256 + wave * 32;   // first token (b * n_k + j) of this wavefront
-    const int tok = tok0 + (lane & 31);
-    const int my_tok = min(tok, ntok - 1);
-    const int b = my_tok / n_k, j = my_tok - b * n_k;
-    const u16* crow = cache + ((int64_t)b * cap + j) * W;
-    bf16x8 cf[KS];
+    const u16* crow = cache_row(tb);
+    bf16x8 cn[KS];
+    {
+      const u16* nrow = cache_row(tb + gridDim.x);
 #pragma unroll
-    for (int k = 0; k < KS; ++k) cf[k] = *reinterpret_cast<const bf16x8*>(crow + k * 16 + half * 8);
+      for (int k = 0; k < KS; ++k) cn[k] = *reinterpret_cast<const bf16x8*>(nrow + k * 16 + half * 8);
+    }
     if (!is_v) {   // the positional key, shared by every head
       const uint4* kr = reinterpret_cast<const uint4*>(crow + DC + half * 16);
       uint4* kd = reinterpret_cast<uint4*>(srow + (DH + half * 16) * 2);
@@ -605,6 +634,8 @@ void mha_uplift_kernel(const u16* __restrict__ cache, int64_t cap, int n_k, int 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int k = 0; k < KS; ++k) cf[k] = cn[k];
   }
 }
 
