@@ -15,16 +15,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Rotation of every (query, rotary pair): cos and sin of the fp64 angle,
-// rounded to fp32 once; shared by all heads and batch samples.
-__global__ __launch_bounds__(256)
-void rope_table_kernel(const int* __restrict__ q_pos, int n_q, int pairs, RopeSpec rope, f32x2* __restrict__ cs) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= n_q * pairs) return;
-  const int i = idx / pairs, pr = idx - i * pairs;
-  const double ang = rope_angle(pr, q_pos[3 * i], q_pos[3 * i + 1], q_pos[3 * i + 2], rope);
-  cs[idx] = f32x2{(float)cos(ang), (float)sin(ang)};
-}
+// 2*pi as an fp64 pair (high part + remainder) and 1/(2*pi), for reducing
+// RoPE angles to [-pi, pi] before the fp32 sine and cosine.
+constexpr double kTwoPiHi = 6.283185307179586232;
+constexpr double kTwoPiLo = 2.4492935982947064e-16;
+constexpr double kInvTwoPi = 0.15915494309189533577;
 
 // One workgroup = 4 wavefronts = 128 queries of one (batch, head).
 // Content part on MFMA: C^T[c][i] = sum_d W_UK[h][d][c] q[i][d].  W_UK[h]
@@ -39,6 +34,12 @@ void rope_table_kernel(const int* __restrict__ q_pos, int n_q, int pairs, RopeSp
 // wavefront's 32 rows of q~ are contiguous in memory and leave as whole
 // 16-byte pieces of consecutive addresses.
 //
+// The positional part rotates q_r by RoPE3D(p_i): the angle p_a * theta^(-2k/d_a)
+// of each pair is formed in fp64 (the 16 inverse frequencies once per
+// workgroup, in LDS), reduced exactly to [-pi, pi] with a two-part 2*pi, and
+// its sine and cosine are taken in fp32.  Their error (about one fp32 ulp) is
+// far below the bf16 rounding of q~ that follows.
+//
 // Workgroup id -> (sample b, head h, query block y): a 128-byte line of q_r
 // holds two heads' 32 values, so the heads 2k and 2k+1 of one query block get
 // ids 8 apart -- the same XCD (workgroups are dealt to the eight XCDs round
@@ -48,7 +49,7 @@ void rope_table_kernel(const int* __restrict__ q_pos, int n_q, int pairs, RopeSp
 template <int DC>
 __global__ __launch_bounds__(256)
 void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
-                        const f32x2* __restrict__ rope_cs, int n_q, int H, int B,
+                        const int* __restrict__ q_pos, RopeSpec rope, int n_q, int H, int B,
                         const u16* __restrict__ w_uk, float qscale,
                         u16* __restrict__ qt, int rows_pad_b) {
   constexpr int DH = 128, DR = 32, W = DC + DR, CB = DC / 32;
@@ -58,6 +59,8 @@ void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
   static_assert(((W * 2 + 16) / 16) & 1, "odd slot stride");
   constexpr int WBYTES = DH * ROWB, OBYTES = 4 * 32 * OROW;
   __shared__ __attribute__((aligned(16))) char wl[WBYTES > OBYTES ? WBYTES : OBYTES];
+  __shared__ double rope_ifreq[DR / 2];
+  __shared__ int rope_axis[DR / 2];
   const int ny = (n_q + 127) / 128, hp = (H + 1) / 2;
   const int u = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
   const int y = u % ny, bk = u / ny, b = bk / hp;
@@ -68,6 +71,11 @@ void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
   const int i = i0 + (lane & 31);
   const bool ok = i < n_q;
 
+  if (threadIdx.x < DR / 2) {
+    int axis;
+    rope_ifreq[threadIdx.x] = rope_inv_freq(threadIdx.x, rope, axis);
+    rope_axis[threadIdx.x] = axis;
+  }
   // A thread's pieces of W_UK[h] and its q row are all loaded before the first
   // LDS store, so the staging costs one round trip, not one per piece.
   constexpr int PER = DH * NCH / 256;                    // 16-byte pieces per thread
@@ -127,7 +135,7 @@ void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
   // Positional part: lane half `half` rotates pairs 8*half .. 8*half+7.
   if (ok) {
     const u16* qr = q_r + qrow_off * DR + half * 16;
-    const f32x2* cs = rope_cs + (int64_t)i * (DR / 2) + half * 8;
+    const int* qp = q_pos + 3 * i;
     const uint4 r0 = *reinterpret_cast<const uint4*>(qr), r1 = *reinterpret_cast<const uint4*>(qr + 8);
     const uint32_t in[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
     uint32_t outw[8];
@@ -135,8 +143,13 @@ void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
     for (int pp = 0; pp < 8; ++pp) {
       const float x0 = __builtin_bit_cast(float, in[pp] << 16);
       const float x1 = __builtin_bit_cast(float, in[pp] & 0xFFFF0000u);
-      const f32x2 r = cs[pp];
-      const float y0 = fmaf(x0, r[0], -(x1 * r[1])), y1 = fmaf(x0, r[1], x1 * r[0]);
+      const int pr = half * 8 + pp;
+      const double ang = (double)qp[rope_axis[pr]] * rope_ifreq[pr];
+      const double k = rint(ang * kInvTwoPi);
+      const float red = (float)fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang));
+      float sn, cs;
+      sincosf(red, &sn, &cs);
+      const float y0 = fmaf(x0, cs, -(x1 * sn)), y1 = fmaf(x0, sn, x1 * cs);
       outw[pp] = bf16x2_bits(to_bf16x2(y0 * qscale, y1 * qscale));
     }
     uint4* o = reinterpret_cast<uint4*>(orow + (DC + half * 16) * 2);
@@ -215,10 +228,6 @@ void absorb_f32_kernel(const float* __restrict__ q, const float* __restrict__ q_
 }
 
 hipError_t launch_absorb_bf16(const Plan& p, const AbsorbArgs& a, hipStream_t s) {
-  const int pairs = (p.width - p.d_c) / 2;
-  f32x2* cs = (f32x2*)a.rope_cs;
-  rope_table_kernel<<<dim3((unsigned)((p.n_q * pairs + 255) / 256)), dim3(256), 0, s>>>(a.q_pos, p.n_q, pairs, a.rope,
-                                                                                         cs);
   const int64_t units = (int64_t)p.B * ((p.H + 1) / 2) * ((p.n_q + 127) / 128);
   const dim3 grid((unsigned)((units + 7) / 8 * 16)), block(256);   // see the id mapping in the kernel
   const u16* q = (const u16*)a.q;
@@ -226,10 +235,10 @@ hipError_t launch_absorb_bf16(const Plan& p, const AbsorbArgs& a, hipStream_t s)
   const u16* wk = (const u16*)a.w_uk;
   u16* qt = (u16*)a.qt;
   switch (p.d_c) {
-    case 64: absorb_bf16_kernel<64><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, p.B, wk, a.qscale, qt, p.rows_pad_b); break;
-    case 128: absorb_bf16_kernel<128><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, p.B, wk, a.qscale, qt, p.rows_pad_b); break;
-    case 192: absorb_bf16_kernel<192><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, p.B, wk, a.qscale, qt, p.rows_pad_b); break;
-    case 256: absorb_bf16_kernel<256><<<grid, block, 0, s>>>(q, qr, cs, p.n_q, p.H, p.B, wk, a.qscale, qt, p.rows_pad_b); break;
+    case 64: absorb_bf16_kernel<64><<<grid, block, 0, s>>>(q, qr, a.q_pos, a.rope, p.n_q, p.H, p.B, wk, a.qscale, qt, p.rows_pad_b); break;
+    case 128: absorb_bf16_kernel<128><<<grid, block, 0, s>>>(q, qr, a.q_pos, a.rope, p.n_q, p.H, p.B, wk, a.qscale, qt, p.rows_pad_b); break;
+    case 192: absorb_bf16_kernel<192><<<grid, block, 0, s>>>(q, qr, a.q_pos, a.rope, p.n_q, p.H, p.B, wk, a.qscale, qt, p.rows_pad_b); break;
+    case 256: absorb_bf16_kernel<256><<<grid, block, 0, s>>>(q, qr, a.q_pos, a.rope, p.n_q, p.H, p.B, wk, a.qscale, qt, p.rows_pad_b); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -91,7 +91,7 @@ struct Plan {
   bool causal;          // per-row-block units (chunk-causal call)
   int32_t elem;         // bytes per element of q~ (2 bf16, 4 f32)
   // byte offsets inside the workspace
-  int64_t off_qt, off_L, off_ml, off_units, off_hdr, off_rope, total;
+  int64_t off_qt, off_L, off_ml, off_units, off_hdr, total;
 };
 
 // The partition the attention kernel used, left in the workspace for the merge.
@@ -182,8 +182,7 @@ inline Plan make_plan(int B, int H, int n_q, int n_k, int d_c, int d_r, bool f32
   int64_t ml_bytes = slots * kRowsPerBlock * 2 * 4;
   p.off_units = align_up(p.off_ml + ml_bytes, 256);
   p.off_hdr = align_up(p.off_units + (int64_t)(p.nrb + 1) * 8, 256);
-  p.off_rope = align_up(p.off_hdr + (int64_t)sizeof(PartitionHeader), 256);   // (cos, sin) per query and pair
-  p.total = align_up(p.off_rope + (int64_t)n_q * (d_r / 2) * 8, 256);
+  p.total = align_up(p.off_hdr + (int64_t)sizeof(PartitionHeader), 256);
   return p;
 }
 
@@ -208,16 +207,23 @@ struct RopeSpec {
   double theta;
 };
 
-// Rotation angle of 3D-RoPE pair `pair` (0 .. d_r/2-1) at position (t,h,w),
-// evaluated in fp64: pair i of an axis of width d_a turns by p_a*theta^(-2i/d_a).
-__device__ inline double rope_angle(int pair, int pt, int ph, int pw, const RopeSpec& r) {
+// Axis (0: t, 1: h, 2: w) and inverse frequency of 3D-RoPE pair `pair` (0 ..
+// d_r/2-1), in fp64: pair i of an axis of width d_a turns by
+// p_a * theta^(-2i/d_a).
+__device__ inline double rope_inv_freq(int pair, const RopeSpec& r, int& axis) {
   const int e = 2 * pair;
-  int width, pos, i;
-  if (e < r.t) { width = r.t; pos = pt; i = pair; }
-  else if (e < r.t + r.h) { width = r.h; pos = ph; i = pair - r.t / 2; }
-  else { width = r.w; pos = pw; i = pair - (r.t + r.h) / 2; }
-  const double inv_freq = pow(r.theta, -2.0 * (double)i / (double)width);
-  return (double)pos * inv_freq;
+  int width, i;
+  if (e < r.t) { width = r.t; axis = 0; i = pair; }
+  else if (e < r.t + r.h) { width = r.h; axis = 1; i = pair - r.t / 2; }
+  else { width = r.w; axis = 2; i = pair - (r.t + r.h) / 2; }
+  return pow(r.theta, -2.0 * (double)i / (double)width);
+}
+
+// Rotation angle of 3D-RoPE pair `pair` at position (t,h,w), in fp64.
+__device__ inline double rope_angle(int pair, int pt, int ph, int pw, const RopeSpec& r) {
+  int axis;
+  const double inv_freq = rope_inv_freq(pair, r, axis);
+  return (double)(axis == 0 ? pt : axis == 1 ? ph : pw) * inv_freq;
 }
 
 }  // namespace mla

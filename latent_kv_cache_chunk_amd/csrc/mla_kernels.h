@@ -22,7 +22,6 @@ struct AbsorbArgs {
   const void* w_uk;
   float qscale;   // softmax_scale * log2(e)
   void* qt;       // workspace + plan.off_qt
-  void* rope_cs;  // workspace + plan.off_rope: float (cos, sin) per query and rotary pair
   RopeSpec rope;
 };
 
