@@ -254,6 +254,32 @@ def test_zero_query_gives_mean_of_values(name):
     assert_g2(got, want, name + " q = 0", max_norm=1e-3, mean_norm=1e-4)
 
 
+@pytest.mark.parametrize("form", ["absorbed", "expanded", "auto"])
+@pytest.mark.parametrize("d_c", [64, 192, 256])
+def test_single_key_gives_that_keys_value(form, d_c):
+    """A one-token chunk with nothing cached (n_q = n_k = 1, the smallest
+    call the ABI takes): the softmax weight is exactly 1, so every head's
+    output is W_UV[h] c_0 whatever the query (a closed form)."""
+    mla = need_gpu()
+    wl = replace(synth.TINY, d_c=d_c, grid_hw=(1, 1), query_frames=(1,), cache_frames=())
+    inp = synth.attend_inputs(wl, seed=21)
+    c0 = np64(inp["cache"])[:, 0, :d_c]                                      # [B, d_c]
+    want = np.einsum("bc,hdc->bhd", c0, np64(inp["w_uv"]))                    # [B, H, d_h]
+    want = np.broadcast_to(want[:, None], (wl.batch, wl.n_q, wl.n_heads, wl.head_dim))
+    d = _dev(inp)
+    fn = {"absorbed": mla.chunk_attend, "expanded": mla.chunk_attend_expanded, "auto": mla.chunk_attend_auto}[form]
+    out = fn(_dims(mla, wl), d["q"], d["q_r"], d["q_pos"], d["w_uk"], d["w_uv"], d["cache"], 1, inp["scale"],
+             out_dtype=torch.float32 if form != "expanded" else None)
+    torch.cuda.synchronize()
+    got = np64(out)
+    if form == "expanded":
+        # bf16 output; V_h = W_UV[h] c_0 is itself rounded to bf16 once
+        assert_g1(got, want, f"single key {form} dc{d_c}")
+    else:
+        # p = 1 exactly, L = c_0 exactly (bf16 hi/lo split exact); only fp32 sums remain
+        assert_g2(got, want, f"single key {form} dc{d_c}", max_norm=1e-4, mean_norm=1e-5)
+
+
 # ------------------------------------------------ composition and hygiene
 def test_steps_compose_to_chunk_attend():
     mla = need_gpu()
