@@ -356,17 +356,21 @@ struct SegmentIter {
   int64_t nrb;
   int64_t rb;
   int t0, t1, b, rbl;
+  // Next segment that holds a key tile (one of start-up units only is skipped).
   __device__ bool next() {
-    if (u_end <= u) return false;
-    rb = rb_of_unit(units, T, nrb, u_end - 1);
-    const int64_t first = rb_first_unit(units, T, rb);
-    const int64_t begin = max(u, first);
-    t0 = (int)(begin - first);
-    t1 = (int)(u_end - first);
-    b = (int)(rb / rb_per_b);
-    rbl = (int)(rb - (int64_t)b * rb_per_b);
-    u_end = begin;
-    return true;
+    while (u < u_end) {
+      rb = rb_of_unit(units, T, nrb, u_end - 1);
+      const int64_t first = rb_first_unit(units, T, rb);
+      const int64_t begin = max(u, first);
+      seg_tiles(units, first, begin, u_end, t0, t1);
+      u_end = begin;
+      if (t1 > t0) {
+        b = (int)(rb / rb_per_b);
+        rbl = (int)(rb - (int64_t)b * rb_per_b);
+        return true;
+      }
+    }
+    return false;
   }
 };
 
@@ -593,14 +597,17 @@ void attend_f32_kernel(const float* __restrict__ cache, int64_t cache_bstride, i
 }
 
 // units[rb] of a chunk-causal call: exclusive prefix sum over row blocks of
-// the key tiles some row of the block can see (Plan), units[nrb] = U.  One
-// workgroup; each thread sums a contiguous run of row blocks.
+// kSegmentUnits plus the key tiles some row of the block can see (Plan),
+// units[nrb] = U.  One workgroup; each thread sums a contiguous run of row
+// blocks.
 __global__ __launch_bounds__(1024)
 void units_kernel(int64_t* __restrict__ units, int nrb, int rb_per_b, int n_k, int bn, Visibility vis) {
   __shared__ int64_t part[1024];
   const int t = threadIdx.x, per = (nrb + 1023) / 1024;
   const int r0 = min(nrb, t * per), r1 = min(nrb, r0 + per);
-  auto tiles = [&](int rb) { return (int64_t)((vis.kv_max_of_block((rb % rb_per_b) * kRowsPerBlock, n_k) + bn - 1) / bn); };
+  auto tiles = [&](int rb) {
+    return (int64_t)((vis.kv_max_of_block((rb % rb_per_b) * kRowsPerBlock, n_k) + bn - 1) / bn) + kSegmentUnits;
+  };
   int64_t sum = 0;
   for (int rb = r0; rb < r1; ++rb) sum += tiles(rb);
   part[t] = sum;

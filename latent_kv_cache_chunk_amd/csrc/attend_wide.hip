@@ -365,8 +365,12 @@ void attend_wide_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstrid
     const int64_t rb = rb_of_unit(units, T, nrb, u_end - 1);
     const int64_t first = rb_first_unit(units, T, rb);
     const int64_t begin = max(u, first);
-    const int t0 = (int)(begin - first);
-    const int t1 = (int)(u_end - first);
+    int t0, t1;
+    seg_tiles(units, first, begin, u_end, t0, t1);
+    if (t1 <= t0) {   // start-up units only: no partial state
+      u_end = begin;
+      continue;
+    }
     const int b = (int)(rb / rb_per_b);
     const int rbl = (int)(rb - (int64_t)b * rb_per_b);
     const char* gbase = reinterpret_cast<const char*>(cache + (int64_t)b * cache_bstride);

@@ -25,6 +25,14 @@ constexpr int kRowsPerBlock = 256;
 __host__ __device__ constexpr int key_tile(int d_c) { return d_c <= 192 ? 64 : 128; }
 // Compute units the work partition is sized for (MI355X).
 constexpr int kPartitionCUs = 256;
+// Start-up cost of a row-block segment, in key tiles of work, for the
+// partition of chunk-causal calls: loading the rows' queries, filling the tile
+// pipeline and writing the partial state (and merging it afterwards).
+// Counting it evens out workgroups that cover many short row blocks against
+// those that cover a few long ones.  At 7 chunks of 4680 queries a segment
+// measures about 26 us of workgroup time (~9 tiles of ~2.8 us); kernel times
+// over the values 4..24 are flat from 12 to 24, and 16 sits in the middle.
+constexpr int kSegmentUnits = 16;
 // Most workgroups that share one row block.  Short chunks (few row blocks)
 // would otherwise spread each row block over up to a hundred workgroups and
 // leave the merge that many partial states per row.
@@ -64,14 +72,18 @@ struct Visibility {
 // Work partition of the fused attention kernel.
 //
 // Units are (row-block, key-tile) pairs.  Every key tile of a row block is a
-// unit (T per row block) unless the call is chunk-causal: then a row block
-// has only the tiles some of its rows can see, and units[rb] (an exclusive
-// prefix sum, in the workspace) gives the first unit of row block rb.  G
-// workgroups each take the contiguous unit range [floor(w*U/G),
-// floor((w+1)*U/G)) and leave one partial softmax state per row block they
-// touch, in slot w + rb: a workgroup's row blocks are consecutive, so these
-// slots are distinct, and fewer than G + nrb.  The merge step finds the
-// owners of a row block's first and last unit arithmetically.
+// unit (T per row block) unless the call is chunk-causal and its row blocks
+// see different numbers of key tiles: then a row block has kSegmentUnits
+// start-up units (no tile) followed by the tiles some of its rows can see,
+// and units[rb] (an exclusive prefix sum, in the workspace) gives the first
+// unit of row block rb; unit first + kSegmentUnits + t is its tile t
+// (seg_tiles below).  G workgroups each take the contiguous unit
+// range [floor(w*U/G), floor((w+1)*U/G)) and leave one partial softmax state
+// per row block whose tiles they touch, in slot w + rb: a workgroup's row
+// blocks are consecutive, so these slots are distinct, and fewer than
+// G + nrb.  The merge step finds the owners of a row block's first key-tile
+// unit and of its last unit arithmetically; every workgroup between them
+// holds some of the row block's tiles (ranges are never empty, as G <= U).
 //
 // A slot holds, for its 256 rows, (m, l) pairs and the unnormalised fp32 L
 // rows.  The bf16 kernels store L channel-quad-major inside each 32-row
@@ -122,6 +134,21 @@ __host__ __device__ inline int64_t rb_of_unit(const int64_t* units, int64_t T, i
   }
   return lo;
 }
+// First unit of row block rb that holds a key tile (the start-up units of a
+// chunk-causal row block hold none).  A workgroup whose part of a row block
+// is start-up units only leaves no partial state for it, so the merge starts
+// at the owner of this unit.
+__host__ __device__ inline int64_t rb_first_tile_unit(const int64_t* units, int64_t T, int64_t rb) {
+  return rb_first_unit(units, T, rb) + (units ? kSegmentUnits : 0);
+}
+// Tiles [t0, t1) of the units [begin, end) of a row block whose first unit is
+// `first` (start-up units of chunk-causal row blocks hold no tile).
+__host__ __device__ inline void seg_tiles(const int64_t* units, int64_t first, int64_t begin, int64_t end, int& t0,
+                                          int& t1) {
+  const int64_t skip = units ? kSegmentUnits : 0;
+  t0 = (int)(begin - first - skip > 0 ? begin - first - skip : 0);
+  t1 = (int)(end - first - skip > 0 ? end - first - skip : 0);
+}
 // Slot of workgroup w's partial state for row block rb.
 __host__ __device__ inline int64_t seg_slot(int64_t w, int64_t rb) { return w + rb; }
 // Float index of channel c of row `row` (0..255) of a slot's L (bf16 kernels):
@@ -134,8 +161,9 @@ inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 // Build the plan.  bf16: stream-K style partition over kPartitionCUs when the
 // plain one-workgroup-per-row-block launch would leave more than 10% of the
-// compute units idle in its last round; chunk-causal calls always spread
-// their (uneven) units over kPartitionCUs workgroups; either way no row block
+// compute units idle in its last round; chunk-causal calls whose row blocks
+// see different numbers of key tiles always spread their units over
+// kPartitionCUs workgroups; either way no row block
 // is split over more than kMaxSplitsPerBlock workgroups.  f32: one workgroup
 // per row-block.  The workspace size does not depend on `vis`.
 inline Plan make_plan(int B, int H, int n_q, int n_k, int d_c, int d_r, bool f32,
@@ -163,10 +191,17 @@ inline Plan make_plan(int B, int H, int n_q, int n_k, int d_c, int d_r, bool f32
   // nrb * kMaxSplitsPerBlock)), so the workspace size does not depend on `vis`.
   const int64_t causal_g = std::min<int64_t>(kPartitionCUs, (int64_t)p.nrb * kMaxSplitsPerBlock);
   const int64_t g_slots = G > causal_g ? G : causal_g;
-  if (!f32 && vis != nullptr && vis->chunk_len != 0) {
+  // A chunk-causal call in which every row block sees every key tile keeps
+  // the plain partition (its rows still mask their own keys), so that it
+  // splits the keys exactly as the unmasked call does.
+  bool uneven = false;
+  if (!f32 && vis != nullptr && vis->chunk_len != 0)
+    for (int rbl = 0; rbl < p.rb_per_b && !uneven; ++rbl)
+      uneven = (vis->kv_max_of_block(rbl * kRowsPerBlock, n_k) + bn - 1) / bn != p.T;
+  if (uneven) {
     int64_t per_b = 0;
     for (int rbl = 0; rbl < p.rb_per_b; ++rbl)
-      per_b += (vis->kv_max_of_block(rbl * kRowsPerBlock, n_k) + bn - 1) / bn;
+      per_b += (vis->kv_max_of_block(rbl * kRowsPerBlock, n_k) + bn - 1) / bn + kSegmentUnits;
     p.U = (int64_t)B * per_b;
     G = p.U < kPartitionCUs ? p.U : kPartitionCUs;
     if (G > (int64_t)p.nrb * kMaxSplitsPerBlock) G = (int64_t)p.nrb * kMaxSplitsPerBlock;

@@ -44,12 +44,12 @@ void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restric
   const int64_t rb = (int64_t)b * rb_per_b + r / kRowsPerBlock;
   const int rl = r % kRowsPerBlock;
 
-  // The attention step's partition; owners of this row-block's first and
-  // last unit, whose segments are merged.
+  // The attention step's partition; owners of this row-block's first
+  // key-tile unit and of its last unit, whose segments are merged.
   const PartitionHeader ph = *hdr;
   const int64_t U = ph.U, G = ph.G;
   const int64_t* units = ph.per_block_units ? units_ws : nullptr;
-  const int64_t u_first = rb_first_unit(units, T, rb), u_last = rb_first_unit(units, T, rb + 1) - 1;
+  const int64_t u_first = rb_first_tile_unit(units, T, rb), u_last = rb_first_unit(units, T, rb + 1) - 1;
   const int64_t wa = unit_owner(u_first, U, G), wb = unit_owner(u_last, U, G);
 
   // W_UV[h] (DH rows of DC bf16) staged once per workgroup by direct-to-LDS

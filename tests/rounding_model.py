@@ -46,6 +46,7 @@ import oracle
 ROWS_PER_BLOCK = 256
 PARTITION_CUS = 256
 MAX_SPLITS = 16
+SEGMENT_UNITS = 16     # start-up units per row block of a chunk-causal partition
 FIRST_BLOCK = 32
 LOG2E = math.log2(math.e)
 
@@ -64,13 +65,8 @@ def kv_of_rows(n_q: int, H: int, n_k: int, causal) -> np.ndarray:
     return np.minimum(n_k, ((q_start + i) // c + 1) * c).astype(np.int64)
 
 
-def split_units(tiles_per_rb, spread: bool) -> list[list[tuple[int, int]]]:
-    """Tile ranges [t0, t1) of every row block's segments.
-
-    tiles_per_rb: units (key tiles) of each row block.  spread: the partition
-    always spreads over the compute units (chunk-causal calls); otherwise it
-    does so only when one workgroup per row block would leave more than 10% of
-    them idle in the last round."""
+def partition_size(tiles_per_rb, spread: bool) -> tuple[int, int]:
+    """(U units, G workgroups) of the partition split_units describes."""
     per = np.asarray(tiles_per_rb, np.int64)
     nrb = per.size
     if spread:
@@ -78,9 +74,28 @@ def split_units(tiles_per_rb, spread: bool) -> list[list[tuple[int, int]]]:
     else:
         rounds = -(-nrb // PARTITION_CUS)
         G = rounds * PARTITION_CUS if nrb / (rounds * PARTITION_CUS) < 0.9 else nrb
-    U = int(per.sum())
-    G = max(1, min(G, U, nrb * MAX_SPLITS))
-    first = np.concatenate([[0], np.cumsum(per)])
+    U = int((per + (SEGMENT_UNITS if spread else 0)).sum())
+    return U, max(1, min(G, U, nrb * MAX_SPLITS))
+
+
+def split_units(tiles_per_rb, spread: bool) -> list[list[tuple[int, int]]]:
+    """Tile ranges [t0, t1) of every row block's segments.
+
+    tiles_per_rb: key tiles of each row block.  spread: a chunk-causal call
+    whose row blocks see different numbers of key tiles.  Its partition always
+    spreads over the compute units, and each row block counts SEGMENT_UNITS
+    start-up units ahead of its tiles (the cost of loading its queries and
+    writing a partial state); a workgroup whose part of a row block is
+    start-up units only leaves no segment for it.  Otherwise
+    a row block has only its tiles, and the partition spreads only when one
+    workgroup per row block would leave more than 10% of the compute units
+    idle in the last round."""
+    per = np.asarray(tiles_per_rb, np.int64)
+    nrb = per.size
+    skip = SEGMENT_UNITS if spread else 0
+    units = per + skip
+    U, G = partition_size(per, spread)
+    first = np.concatenate([[0], np.cumsum(units)])
     bounds = [(w * U) // G for w in range(G + 1)]
     out = []
     for rb in range(nrb):
@@ -88,11 +103,12 @@ def split_units(tiles_per_rb, spread: bool) -> list[list[tuple[int, int]]]:
         w0 = max(0, int(np.searchsorted(bounds, u0, side="right")) - 1)
         segs = []
         for w in range(w0, G):
-            a, b = max(u0, bounds[w]), min(u1, bounds[w + 1])
             if bounds[w] >= u1:
                 break
-            if a < b:
-                segs.append((a - u0, b - u0))
+            a = max(u0, bounds[w]) - u0 - skip
+            b = min(u1, bounds[w + 1]) - u0 - skip
+            if b > max(a, 0):
+                segs.append((max(a, 0), b))
         out.append(segs)
     return out
 
@@ -148,7 +164,9 @@ def attend(q, q_r, q_pos, w_uk, w_uv, cache, n_k: int, scale: float, split=(8, 1
     rows_b = H * n_q
     rb_per_b = -(-rows_b // ROWS_PER_BLOCK)
     per = [-(-int(kv[r * ROWS_PER_BLOCK: (r + 1) * ROWS_PER_BLOCK].max()) // bn) for r in range(rb_per_b)]
-    segs = split_units(per * B, spread=causal is not None)
+    # a chunk-causal call takes the uneven partition only when its row blocks
+    # see different numbers of key tiles
+    segs = split_units(per * B, spread=causal is not None and any(t != -(-n_k // bn) for t in per))
     keys = np.arange(n_k)
     out = np.empty((B, n_q, H, d_h))
     for b in range(B):

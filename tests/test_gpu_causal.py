@@ -161,3 +161,42 @@ def test_480p_teacher_forcing_sampled_rows():
     got = _gpu(mla, wl, inp, causal, out_dtype=torch.float32)
     assert_g2(got[rows[:, 0], rows[:, 1], rows[:, 2]], _oracle_rows(wl, inp, causal, rows), "480p tf",
               max_norm=G2_CAUSAL_MAX)
+
+
+@pytest.mark.parametrize("name,causal", [("tiny_all", (0, 48)), ("mid_all", (0, 2 * 192)),
+                                         ("wan480p_tf", (0, 4680))])
+def test_partition_header_matches_model(name, causal):
+    """The attention kernel leaves its partition (U units, G workgroups) in the
+    last 256 bytes of the workspace for the merge; the rounding model in
+    tests/rounding_model.py splits row blocks the same way, so its U and G
+    must be the kernel's: key tiles plus start-up units per row block when the
+    row blocks see different numbers of tiles, else the plain partition."""
+    import tests.rounding_model as rm
+    mla = need_gpu()
+    wl = {"tiny_all": TINY_ALL,
+          "mid_all": replace(synth.TINY, name="mid_all", grid_hw=(12, 16), cache_frames=(),
+                             query_frames=tuple(range(12))),
+          "wan480p_tf": replace(synth.WAN480P, name="wan480p_tf", cache_frames=(),
+                                query_frames=tuple(range(21)))}[name]
+    inp = synth.attend_inputs(wl, seed=0)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    dims = _dims(mla, wl)
+    ws = mla.alloc_workspace(dims, torch.bfloat16, wl.n_q, inp["n_k"], "cuda")
+    ws.fill_(0xFF)
+    mla.chunk_attend(dims, d["q"], d["q_r"], d["q_pos"], d["w_uk"], d["w_uv"], d["cache"], inp["n_k"],
+                     inp["scale"], workspace=ws, causal=causal)
+    torch.cuda.synchronize()
+    tail = ws.view(torch.uint8)[-256:-240].cpu().numpy()
+    U, = tail[:8].view(np.int64)
+    G, per_block = tail[8:16].view(np.int32)
+
+    kv = rm.kv_of_rows(wl.n_q, wl.n_heads, inp["n_k"], causal)
+    rb_per_b = -(-kv.size // rm.ROWS_PER_BLOCK)
+    bn = rm.latent_tile(wl.d_c)
+    tiles = [-(-int(kv[r * rm.ROWS_PER_BLOCK:(r + 1) * rm.ROWS_PER_BLOCK].max()) // bn) for r in range(rb_per_b)]
+    uneven = any(t != -(-inp["n_k"] // bn) for t in tiles)
+    assert uneven == (name != "tiny_all")   # tiny_all: every row block holds a row of the last chunk
+    want_U, want_G = rm.partition_size(tiles * wl.batch, spread=uneven)
+    assert (int(U), int(G), int(per_block)) == (want_U, want_G, int(uneven))
+    segs = rm.split_units(tiles * wl.batch, spread=uneven)
+    assert all(sorted(t for a, b in sg for t in range(a, b)) == list(range(n)) for sg, n in zip(segs, tiles))
