@@ -297,6 +297,32 @@ def test_steps_compose_to_chunk_attend():
     assert torch.equal(full.view(torch.int16), out.view(torch.int16))
 
 
+@pytest.mark.parametrize("causal", [None, (1500, 300), (1200, 150)])
+def test_attend_twice_after_one_absorb(causal):
+    """Attention and up-projection read nothing of the workspace but the absorbed
+    queries and what the attention call itself writes (partial states, the
+    partition header, the per-row-block units): repeating them on the same
+    absorbed queries, over a workspace that started as garbage, must give the
+    fused call's bits every time."""
+    mla = need_gpu()
+    wl = replace(synth.TINY, grid_hw=(30, 10), query_frames=(6,), cache_frames=tuple(range(6)))
+    inp = _dev(synth.attend_inputs(wl, seed=13))
+    d = _dims(mla, wl)
+    ws = mla.alloc_workspace(d, torch.bfloat16, wl.n_q, wl.n_k)
+    ws.fill_(0x55)
+    outs = [torch.empty((1, wl.n_q, wl.n_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    mla.query_absorb(d, inp["q"], inp["q_r"], inp["q_pos"], inp["w_uk"], wl.scale, wl.n_k, ws)
+    for o in outs:
+        mla.latent_attend(d, inp["cache"], wl.n_q, wl.n_k, ws, causal=causal)
+        mla.value_upproj(d, inp["w_uv"], o, wl.n_q, wl.n_k, ws)
+    full = mla.chunk_attend(d, inp["q"], inp["q_r"], inp["q_pos"], inp["w_uk"], inp["w_uv"], inp["cache"],
+                            wl.n_k, wl.scale, causal=causal)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), full.view(torch.int16))
+    assert torch.isfinite(full.float()).all()
+
+
 def test_deterministic_and_poisoned_workspace():
     mla = need_gpu()
     wl = replace(synth.TINY, grid_hw=(30, 10), query_frames=(6,), cache_frames=tuple(range(6)))
