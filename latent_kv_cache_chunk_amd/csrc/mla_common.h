@@ -26,12 +26,15 @@ __host__ __device__ constexpr int key_tile(int d_c) { return d_c <= 192 ? 64 : 1
 // Compute units the work partition is sized for (MI355X).
 constexpr int kPartitionCUs = 256;
 // Start-up cost of a row-block segment, in key tiles of work, for the
-// partition of chunk-causal calls: loading the rows' queries, filling the tile
-// pipeline and writing the partial state (and merging it afterwards).
-// Counting it evens out workgroups that cover many short row blocks against
-// those that cover a few long ones.  At 7 chunks of 4680 queries a segment
-// measures about 26 us of workgroup time (~9 tiles of ~2.8 us); kernel times
-// over the values 4..24 are flat from 12 to 24, and 16 sits in the middle.
+// partition of chunk-causal calls: loading the rows' queries, filling and
+// draining the tile pipeline, writing the partial state (and merging it
+// afterwards).  Counting it evens out workgroups that cover many short row
+// blocks against those that cover a few long ones.  At 7 chunks of 4680
+// queries a probe build timed each segment's sweep at 5.9 us + 2.53 us per
+// tile, with 3.0 us before it and 5.6 us after it: about 14.5 us, six tiles,
+// of fixed cost.  Kernel times over the values 4..24 are flat from 12 to 24
+// (the merge's extra states and the row blocks' L2 drift also grow with the
+// segment count), and 16 sits in the middle.
 constexpr int kSegmentUnits = 16;
 // Most workgroups that share one row block.  Short chunks (few row blocks)
 // would otherwise spread each row block over up to a hundred workgroups and

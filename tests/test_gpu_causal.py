@@ -163,9 +163,15 @@ def test_480p_teacher_forcing_sampled_rows():
               max_norm=G2_CAUSAL_MAX)
 
 
-@pytest.mark.parametrize("name,causal", [("tiny_all", (0, 48)), ("mid_all", (0, 2 * 192)),
-                                         ("wan480p_tf", (0, 4680))])
-def test_partition_header_matches_model(name, causal):
+@pytest.mark.parametrize("name,causal,uneven_rbs", [
+    ("tiny_all", (0, 48), False),          # every row block holds a row of the last chunk
+    ("mid_all", (0, 2 * 192), True),
+    ("wan480p_tf", (0, 4680), True),
+    ("wan480p", None, False),              # 220 row blocks: stream-K over 256 workgroups
+    ("wan480p_shard8", None, False),       # 28 row blocks: up to 16 workgroups each
+    ("wan480p_b8", None, False),           # 1760 row blocks fill 7 rounds: one workgroup each
+])
+def test_partition_header_matches_model(name, causal, uneven_rbs):
     """The attention kernel leaves its partition (U units, G workgroups) in the
     last 256 bytes of the workspace for the merge; the rounding model in
     tests/rounding_model.py splits row blocks the same way, so its U and G
@@ -177,7 +183,7 @@ def test_partition_header_matches_model(name, causal):
           "mid_all": replace(synth.TINY, name="mid_all", grid_hw=(12, 16), cache_frames=(),
                              query_frames=tuple(range(12))),
           "wan480p_tf": replace(synth.WAN480P, name="wan480p_tf", cache_frames=(),
-                                query_frames=tuple(range(21)))}[name]
+                                query_frames=tuple(range(21)))}.get(name) or synth.WORKLOADS[name]
     inp = synth.attend_inputs(wl, seed=0)
     d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     dims = _dims(mla, wl)
@@ -195,7 +201,7 @@ def test_partition_header_matches_model(name, causal):
     bn = rm.latent_tile(wl.d_c)
     tiles = [-(-int(kv[r * rm.ROWS_PER_BLOCK:(r + 1) * rm.ROWS_PER_BLOCK].max()) // bn) for r in range(rb_per_b)]
     uneven = any(t != -(-inp["n_k"] // bn) for t in tiles)
-    assert uneven == (name != "tiny_all")   # tiny_all: every row block holds a row of the last chunk
+    assert uneven == uneven_rbs
     want_U, want_G = rm.partition_size(tiles * wl.batch, spread=uneven)
     assert (int(U), int(G), int(per_block)) == (want_U, want_G, int(uneven))
     segs = rm.split_units(tiles * wl.batch, spread=uneven)
