@@ -138,6 +138,24 @@ def test_multi_block_stream_k():
     assert np.all(np.isfinite(got))
 
 
+@pytest.mark.parametrize("d_c", [64, 128, 256])
+def test_multi_block_uneven_partition_dc(d_c):
+    """The uneven (start-up unit) partition at every other latent width: row blocks
+    see different numbers of key tiles, workgroups skip the start-up-only parts
+    of row blocks, and the merge starts at each row block's first key-tile owner.
+    d_c = 256 runs the single-role kernel with its 128-key tiles."""
+    mla = need_gpu()
+    wl = replace(synth.TINY, name="mid_all", grid_hw=(12, 16), cache_frames=(), query_frames=tuple(range(12)),
+                 d_c=d_c)
+    inp = synth.attend_inputs(wl, seed=14)
+    causal = (0, 2 * 192)
+    rows = np.array([[0, i, h] for h in (0, 7, 11) for i in range(0, wl.n_q, 23)] + [[0, wl.n_q - 1, 4]])
+    got = _gpu(mla, wl, inp, causal, out_dtype=torch.float32)
+    assert_g2(got[rows[:, 0], rows[:, 1], rows[:, 2]], _oracle_rows(wl, inp, causal, rows), f"mid dc{d_c}",
+              max_norm=G2_CAUSAL_MAX)
+    assert np.all(np.isfinite(got))
+
+
 @pytest.mark.parametrize("headroom", ["0"])
 def test_two_pass_fallback_causal(monkeypatch, headroom):
     mla = need_gpu()
