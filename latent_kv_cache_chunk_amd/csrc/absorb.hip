@@ -87,12 +87,19 @@ void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
     const int idx = threadIdx.x + 256 * k, r = idx / NCH, ch = idx - r * NCH;
     wv[k] = *reinterpret_cast<const uint4*>(wk + r * DC + ch * 8);
   }
-  const int64_t qrow_off = (((int64_t)b * n_q + (ok ? i : 0)) * H + h);
+  const int ic = ok ? i : 0;
+  const int64_t qrow_off = (((int64_t)b * n_q + ic) * H + h);
   const u16* qrow = q + qrow_off * DH + half * 8;
   bf16x8 qf[DH / 16];
 #pragma unroll
   for (int ks = 0; ks < DH / 16; ++ks)
     qf[ks] = ok ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16) : bf16x8{};
+  // The positional inputs (this lane half's 16 q_r values and the query's
+  // position) load with the rest, so the rotation after the product does not
+  // wait on another round trip.
+  const u16* qr = q_r + qrow_off * DR + half * 16;
+  uint4 r0 = *reinterpret_cast<const uint4*>(qr), r1 = *reinterpret_cast<const uint4*>(qr + 8);
+  int pt = q_pos[3 * ic], ph = q_pos[3 * ic + 1], pw = q_pos[3 * ic + 2];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int idx = threadIdx.x + 256 * k, r = idx / NCH, ch = idx - r * NCH;
@@ -100,8 +107,13 @@ void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
     *reinterpret_cast<uint4*>(wl + rs * ROWB + ch * 16) = wv[k];
   }
   // pin that order (the scheduler otherwise pairs each load with its store)
-  __builtin_amdgcn_sched_group_barrier(0x020, PER + DH / 16, 0);
+  __builtin_amdgcn_sched_group_barrier(0x020, PER + DH / 16 + 5, 0);
   __builtin_amdgcn_sched_group_barrier(0x200, PER, 0);
+  // Keeps the positional loads here (the compiler would otherwise sink them to
+  // their use after the product); every load of the thread has landed by the
+  // barrier below anyway.
+  asm volatile("" : "+v"(r0.x), "+v"(r0.y), "+v"(r0.z), "+v"(r0.w), "+v"(r1.x), "+v"(r1.y), "+v"(r1.z),
+               "+v"(r1.w), "+v"(pt), "+v"(ph), "+v"(pw));
   __syncthreads();
 
   const int g = lane >> 4, j = lane & 15;
@@ -134,9 +146,6 @@ void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
     }
   // Positional part: lane half `half` rotates pairs 8*half .. 8*half+7.
   if (ok) {
-    const u16* qr = q_r + qrow_off * DR + half * 16;
-    const int* qp = q_pos + 3 * i;
-    const uint4 r0 = *reinterpret_cast<const uint4*>(qr), r1 = *reinterpret_cast<const uint4*>(qr + 8);
     const uint32_t in[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
     uint32_t outw[8];
 #pragma unroll
@@ -144,7 +153,8 @@ void absorb_bf16_kernel(const u16* __restrict__ q, const u16* __restrict__ q_r,
       const float x0 = __builtin_bit_cast(float, in[pp] << 16);
       const float x1 = __builtin_bit_cast(float, in[pp] & 0xFFFF0000u);
       const int pr = half * 8 + pp;
-      const double ang = (double)qp[rope_axis[pr]] * rope_ifreq[pr];
+      const int ax = rope_axis[pr];
+      const double ang = (double)(ax == 0 ? pt : ax == 1 ? ph : pw) * rope_ifreq[pr];
       const double k = rint(ang * kInvTwoPi);
       const float red = (float)fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang));
       float sn, cs;
