@@ -357,9 +357,11 @@ struct SegmentIter {
   int64_t rb;
   int t0, t1, b, rbl;
   // Next segment that holds a key tile (one of start-up units only is skipped).
+  // After the first, each segment lies in the row block before the last one:
+  // row blocks are contiguous and never empty.
   __device__ bool next() {
     while (u < u_end) {
-      rb = rb_of_unit(units, T, nrb, u_end - 1);
+      rb = rb < 0 ? rb_of_unit(units, T, nrb, u_end - 1) : rb - 1;
       const int64_t first = rb_first_unit(units, T, rb);
       const int64_t begin = max(u, first);
       seg_tiles(units, first, begin, u_end, t0, t1);
@@ -532,6 +534,7 @@ void attend_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstride, in
   it.rb_per_b = rb_per_b;
   it.units = units;
   it.nrb = nrb;
+  it.rb = -1;
   if (blockIdx.x == 0 && threadIdx.x == 0) *hdr = PartitionHeader{U, G, units != nullptr ? 1 : 0};
   if (scorer)
     score_role<DC>(c, it, cache, cache_bstride, qt, rows_pad_b, part_ml, w, headroom, vis, kbuf0, kbuf1, kbuf2,

@@ -358,11 +358,13 @@ void attend_wide_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstrid
   WaveState<DC, QB> st;
   if (blockIdx.x == 0 && threadIdx.x == 0) *hdr = PartitionHeader{U, G, units != nullptr ? 1 : 0};
 
+  int64_t rb = -1;
   while (u < u_end) {
     // this segment: the part of the range inside one row block (see Plan),
     // last row block first, so that ranges crossing a boundary start at key
-    // tile 0 and the workgroups of an XCD sweep the cache nearly in step
-    const int64_t rb = rb_of_unit(units, T, nrb, u_end - 1);
+    // tile 0 and the workgroups of an XCD sweep the cache nearly in step;
+    // after the first, the row block before (row blocks are never empty)
+    rb = rb < 0 ? rb_of_unit(units, T, nrb, u_end - 1) : rb - 1;
     const int64_t first = rb_first_unit(units, T, rb);
     const int64_t begin = max(u, first);
     int t0, t1;

@@ -36,9 +36,11 @@ constexpr int kPartitionCUs = 256;
 // (the merge's extra states and the row blocks' L2 drift also grow with the
 // segment count), and 16 sits in the middle.
 constexpr int kSegmentUnits = 16;
-// Most workgroups that share one row block.  Short chunks (few row blocks)
-// would otherwise spread each row block over up to a hundred workgroups and
-// leave the merge that many partial states per row.
+// Workgroups per row block, at most, on average: G <= kMaxSplitsPerBlock *
+// nrb.  Short chunks (few row blocks) would otherwise spread each row block
+// over up to a hundred workgroups and leave the merge that many partial
+// states per row.  (Equal row blocks then meet at most 17 workgroups each;
+// a long row block of a chunk-causal call can meet a few more.)
 constexpr int kMaxSplitsPerBlock = 16;
 // log2(e): softmax runs in base 2 with this folded into the query scale.
 constexpr double kLog2e = 1.4426950408889634074;
@@ -166,9 +168,9 @@ inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 // plain one-workgroup-per-row-block launch would leave more than 10% of the
 // compute units idle in its last round; chunk-causal calls whose row blocks
 // see different numbers of key tiles always spread their units over
-// kPartitionCUs workgroups; either way no row block
-// is split over more than kMaxSplitsPerBlock workgroups.  f32: one workgroup
-// per row-block.  The workspace size does not depend on `vis`.
+// kPartitionCUs workgroups; either way G is at most kMaxSplitsPerBlock per
+// row block.  f32: one workgroup per row-block.  The workspace size does not
+// depend on `vis`.
 inline Plan make_plan(int B, int H, int n_q, int n_k, int d_c, int d_r, bool f32,
                       const Visibility* vis = nullptr) {
   Plan p{};
