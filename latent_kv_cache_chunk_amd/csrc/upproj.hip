@@ -78,35 +78,65 @@ void upproj_bf16_kernel(const float* __restrict__ part_L, const float* __restric
   // L of this lane's row and columns {ks*16 + half*8 + e}, merged over the
   // segments in one pass with a running max M: what is summed so far is
   // rescaled by 2^(M_old - M_new) when a segment raises it.  A segment with
-  // no visible key of the row has m = -inf and weight 0.  One segment's
-  // loads at a time keep the wavefront at two per SIMD (rows of short chunks
-  // can have over a hundred segments).
+  // no visible key of the row has m = -inf and weight 0.  At d_c >= 192 the
+  // segments go two at a time, both segments' loads in flight together (still
+  // two wavefronts per SIMD at d_c = 192; the narrower widths would lose a
+  // wavefront per SIMD to it), which halves the serial round trips of rows
+  // with many segments (about ten per row for a short query shard); an odd
+  // last segment goes alone.  The update runs segment by segment in
+  // workgroup order either way.
   float M = -INFINITY, lsum = 0.f;
   float lc[KSTEPS][8];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) lc[ks][e] = 0.f;
-#pragma unroll 1
-  for (int64_t w = active ? wa : wb + 1; w <= wb; ++w) {
+  auto merge = [&](const auto& segs_ml, const auto& x, int nseg) {
+#pragma unroll
+    for (int sg = 0; sg < nseg; ++sg) {
+      const float m_w = segs_ml[sg][0], l_w = segs_ml[sg][1];
+      const float m_new = fmaxf(M, m_w);
+      const float keep = M == -INFINITY ? 0.f : exp2f(M - m_new);
+      const float wgt = m_w == -INFINITY ? 0.f : exp2f(m_w - m_new);
+      M = m_new;
+      lsum = fmaf(lsum, keep, wgt * l_w);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lc[ks][e] = fmaf(wgt, x[sg][ks][0][e], lc[ks][e] * keep);
+          lc[ks][4 + e] = fmaf(wgt, x[sg][ks][1][e], lc[ks][4 + e] * keep);
+        }
+    }
+  };
+  auto load = [&](int64_t w, float (&ml)[2], f32x4 (&x)[KSTEPS][2]) {
     const int64_t sl = seg_slot(w, rb);
-    const float m_w = part_ml[(sl * kRowsPerBlock + rl) * 2], l_w = part_ml[(sl * kRowsPerBlock + rl) * 2 + 1];
-    const float m_new = fmaxf(M, m_w);
-    const float keep = M == -INFINITY ? 0.f : exp2f(M - m_new);
-    const float wgt = m_w == -INFINITY ? 0.f : exp2f(m_w - m_new);
-    M = m_new;
-    lsum = fmaf(lsum, keep, wgt * l_w);
+    ml[0] = part_ml[(sl * kRowsPerBlock + rl) * 2];
+    ml[1] = part_ml[(sl * kRowsPerBlock + rl) * 2 + 1];
     const float* src = part_L + part_L_index(sl, rl, half * 8, DC);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + ks * 512);         // channels ks*16 + half*8 + 0..3
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + ks * 512 + 128);   // channels ks*16 + half*8 + 4..7
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lc[ks][e] = fmaf(wgt, x0[e], lc[ks][e] * keep);
-        lc[ks][4 + e] = fmaf(wgt, x1[e], lc[ks][4 + e] * keep);
-      }
+      x[ks][0] = *reinterpret_cast<const f32x4*>(src + ks * 512);         // channels ks*16 + half*8 + 0..3
+      x[ks][1] = *reinterpret_cast<const f32x4*>(src + ks * 512 + 128);   // channels ks*16 + half*8 + 4..7
     }
+  };
+  int64_t w = active ? wa : wb + 1;
+  if constexpr (DC >= 192) {
+#pragma unroll 1
+    for (; w + 1 <= wb; w += 2) {
+      float ml[2][2];
+      f32x4 x[2][KSTEPS][2];
+      load(w, ml[0], x[0]);
+      load(w + 1, ml[1], x[1]);
+      merge(ml, x, 2);
+    }
+  }
+#pragma unroll 1
+  for (; w <= wb; ++w) {
+    float ml[1][2];
+    f32x4 x[1][KSTEPS][2];
+    load(w, ml[0], x[0]);
+    merge(ml, x, 1);
   }
   const float inv_l = 1.f / lsum;
   __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0): this wavefront's W_UV loads have landed
