@@ -179,7 +179,11 @@ struct ScoreState {
 constexpr int kScorePrefetch = 4;     // score operand loads in flight ahead of their MFMAs
 
 // Scores, softmax and P of every block of tile t (LDS `tile`), P to `pbuf`.
-template <int DC, Pass P>
+// MASK: some key of the tile is past n_k or past a row's visible keys.  The
+// unmasked form has no masking branch after its products, so the scores
+// stay in the registers the products wrote (a branch that may rewrite them
+// made the compiler copy all 32 after every tile's second block).
+template <int DC, Pass P, bool MASK>
 __device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile, char* pbuf, int t, bool first_tile,
                                            const SweepCtx& c) {
   using L = AttendTile<DC>;
@@ -196,7 +200,7 @@ __device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile,
   for (int i = 0; i < PF; ++i) a[i] = *reinterpret_cast<const bf16x8*>(tile + c.s_off + i * 32);
 #pragma unroll
   for (int kb = 0; kb < L::NBLK; ++kb) {
-    if (kb > 0 && kb * 32 >= left) break;
+    if (MASK && kb > 0 && kb * 32 >= left) break;
     f32x16 s[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) s[qb] = f32x16{};
@@ -217,14 +221,16 @@ __device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile,
       if (kb * KS + ks + PF < L::NBLK * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     const int key0 = t * L::BN + kb * 32;
-    if (c.causal) {
-      if (key0 + 32 > c.kv_min) {   // some row of the wavefront ends inside this block
+    if constexpr (MASK) {
+      if (c.causal) {
+        if (key0 + 32 > c.kv_min) {   // some row of the wavefront ends inside this block
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) mask_block(s[qb], c.kv[qb] - key0, c.half);
+          for (int qb = 0; qb < NQB; ++qb) mask_block(s[qb], c.kv[qb] - key0, c.half);
+        }
+      } else if (left - kb * 32 < 32) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) mask_block(s[qb], left - kb * 32, c.half);
       }
-    } else if (left - kb * 32 < 32) {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) mask_block(s[qb], left - kb * 32, c.half);
     }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -315,7 +321,15 @@ __device__ __forceinline__ bool sweep_step(State& st, int k, int n, int t0, char
                                            char* pbuf, const SweepCtx& c) {
   if (!SCORE && k + 1 < n) issue_tile<DC>(c, t0 + k + 1, nxt);
   if constexpr (SCORE) {
-    if (k < n) score_tile<DC, P>(st, cur, pbuf + ((k & 1) ? AttendTile<DC>::PBUF : 0), t0 + k, k == 0, c);
+    if (k < n) {
+      constexpr int BN = AttendTile<DC>::BN;
+      const int t = t0 + k;
+      char* pb = pbuf + ((k & 1) ? AttendTile<DC>::PBUF : 0);
+      if (c.causal ? t * BN + BN > c.kv_min : c.n_k - t * BN < BN)
+        score_tile<DC, P, true>(st, cur, pb, t, k == 0, c);
+      else
+        score_tile<DC, P, false>(st, cur, pb, t, k == 0, c);
+    }
   } else {
     if (P != Pass::kMax && k >= 1) value_tile<DC>(st, prv, pbuf + ((k & 1) ? 0 : AttendTile<DC>::PBUF), t0 + k - 1, c);
   }
