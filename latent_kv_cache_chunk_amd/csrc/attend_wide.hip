@@ -114,11 +114,14 @@ struct WaveState {
 
 enum class Pass { kSingle, kMax, kAccum };
 
-// Scores of one 32-key block for the wave's row blocks.  The k-steps feed two
-// independent accumulator chains per row block (summed at the end) so that
-// consecutive MFMAs never wait on each other's results, and the LDS operand
-// loads run PF k-steps ahead of the MFMA that uses them.
-template <int DC, int QB, int CHAINS = 2>
+// Scores of one 32-key block for the wave's row blocks, the LDS operand loads
+// PF k-steps ahead of the MFMA that uses them.  One accumulator chain per row
+// block: a second, independent chain (summed at the end) spared consecutive
+// MFMAs the wait on each other's results, but its 16 registers pushed two
+// query fragments out to scratch, and their reloads (a vmcnt(0) wait, which
+// also waits for the next tile's loads) sat in every block: 1.77 -> 1.68 ms
+// at 480P without it.
+template <int DC, int QB, int CHAINS = 1>
 __device__ __forceinline__ void block_scores(const WaveState<DC, QB>& st, const char* kbase, f32x16 (&s)[QB]) {
   constexpr int KS = WaveState<DC, QB>::KS;
   constexpr int PF = 4;
