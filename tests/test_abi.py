@@ -207,13 +207,14 @@ def test_chunk_attend_form_rule():
     form = lambda d, dt, n_q, n_k=32760: lib.mla_chunk_attend_form(ctypes.byref(d), dt, n_q, n_k)
     d192 = _dims()
     assert form(d192, 0, 4680) == 1                     # 480P chunk: non-absorbed (4864 rows per head)
-    assert form(d192, 0, 3120) == 1
-    assert form(d192, 0, 1560) == 0                     # below 2048 queries
-    assert form(d192, 0, 2047) == 0
-    assert form(d192, 0, 2048) == 1
+    assert form(d192, 0, 1560) == 1
+    assert form(d192, 0, 1151) == 0                     # below 1152 queries at d_c = 192
+    assert form(d192, 0, 1152) == 1
     assert form(d192, 1, 4680) == 0                     # fp32 inputs: absorbed only
-    assert form(_dims(d_c=128), 0, 4680) == 0
+    assert form(_dims(d_c=128), 0, 4680) == 0           # d_c <= 128: absorbed at every size
     assert form(_dims(d_c=256), 0, 4680) == 1
+    assert form(_dims(d_c=256), 0, 447) == 0            # below 448 queries at d_c = 256
+    assert form(_dims(d_c=256), 0, 448) == 1
     assert form(d192, 0, 0) == -1                       # arguments mla_chunk_attend rejects
     ws_auto = lib.mla_chunk_attend_auto_workspace_bytes(ctypes.byref(d192), 0, 4680, 32760)
     assert ws_auto == lib.mla_chunk_attend_expanded_workspace_bytes(ctypes.byref(d192), 4680, 32760)
