@@ -399,6 +399,24 @@ __device__ __forceinline__ int visible_end(const SegmentIter& it, const Visibili
   return min(it.t1, (kv + BN - 1) / BN);
 }
 
+// OR of `v` over the workgroup with one barrier: each wavefront posts its own
+// vote in one of two LDS vote sets (alternating per call, so a set is
+// rewritten only after every wavefront has passed the next call's barrier,
+// i.e. has read it), then every thread reads all votes.
+template <int NW>
+__device__ __forceinline__ bool workgroup_any(bool v, int* votes, int& parity) {
+  const int wave = threadIdx.x >> 6;
+  const int any = __any(v) ? 1 : 0;
+  int* set = votes + parity * NW;
+  if ((threadIdx.x & 63) == 0) set[wave] = any;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) r |= set[w];
+  parity ^= 1;
+  return r != 0;
+}
+
 __device__ __forceinline__ int wave_min(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
@@ -409,10 +427,12 @@ template <int DC>
 __device__ __forceinline__ void score_role(SweepCtx& c, SegmentIter it, const u16* __restrict__ cache,
                                            int64_t cache_bstride, const u16* __restrict__ qt, int rows_pad_b,
                                            float* __restrict__ part_ml, int64_t w, float headroom,
-                                           const Visibility& vis, char* k0, char* k1, char* k2, char* pbuf) {
+                                           const Visibility& vis, char* k0, char* k1, char* k2, char* pbuf,
+                                           int* votes) {
   using L = AttendTile<DC>;
   constexpr int NQB = ScoreState<DC>::NQB;
   ScoreState<DC> st;
+  int parity = 0;
   while (it.next()) {
     c.gbase = reinterpret_cast<const char*>(cache + (int64_t)it.b * cache_bstride);
     const int te = visible_end<DC>(it, vis, c.n_k);
@@ -433,7 +453,7 @@ __device__ __forceinline__ void score_role(SweepCtx& c, SegmentIter it, const u1
     bool over = false;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) over |= !(st.l_run[qb] <= lim);
-    if (__syncthreads_or(over)) {
+    if (workgroup_any<attend_waves<DC>()>(over, votes, parity)) {
       // A running sum rose past 2^headroom: exact two-pass evaluation.
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) st.m_ref[qb] = -INFINITY;
@@ -458,9 +478,11 @@ __device__ __forceinline__ void score_role(SweepCtx& c, SegmentIter it, const u1
 template <int DC>
 __device__ __forceinline__ void value_role(SweepCtx& c, SegmentIter it, const u16* __restrict__ cache,
                                            int64_t cache_bstride, float* __restrict__ part_L, int64_t w,
-                                           const Visibility& vis, char* k0, char* k1, char* k2, char* pbuf) {
+                                           const Visibility& vis, char* k0, char* k1, char* k2, char* pbuf,
+                                           int* votes) {
   using L = AttendTile<DC>;
   ValueState<DC> st;
+  int parity = 0;
   while (it.next()) {
     c.gbase = reinterpret_cast<const char*>(cache + (int64_t)it.b * cache_bstride);
     const int te = visible_end<DC>(it, vis, c.n_k);
@@ -476,7 +498,7 @@ __device__ __forceinline__ void value_role(SweepCtx& c, SegmentIter it, const u1
       for (int cb = 0; cb < L::CB; ++cb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) bad |= !(fabsf(st.oacc[qb][cb][v]) <= 3.0e38f);
-    if (__syncthreads_or(bad)) {
+    if (workgroup_any<attend_waves<DC>()>(bad, votes, parity)) {
       sweep<DC, Pass::kMax, false>(st, k0, k1, k2, pbuf, it.t0, te, c);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
@@ -519,6 +541,7 @@ void attend_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstride, in
   // a pointer chosen between two objects would not be known to miss the key
   // buffers, and the compiler would wait for the in-flight tile loads first.
   __shared__ __attribute__((aligned(1024))) char pbuf[2 * L::PBUF];
+  __shared__ int votes[2 * attend_waves<DC>()];   // per-segment fallback vote (two alternating sets)
 
   SweepCtx c;
   c.n_k = n_k;
@@ -552,9 +575,9 @@ void attend_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstride, in
   if (blockIdx.x == 0 && threadIdx.x == 0) *hdr = PartitionHeader{U, G, units != nullptr ? 1 : 0};
   if (scorer)
     score_role<DC>(c, it, cache, cache_bstride, qt, rows_pad_b, part_ml, w, headroom, vis, kbuf0, kbuf1, kbuf2,
-                   pbuf);
+                   pbuf, votes);
   else
-    value_role<DC>(c, it, cache, cache_bstride, part_L, w, vis, kbuf0, kbuf1, kbuf2, pbuf);
+    value_role<DC>(c, it, cache, cache_bstride, part_L, w, vis, kbuf0, kbuf1, kbuf2, pbuf, votes);
 }
 
 // fp32 variant: 8 threads per row, 32 rows per workgroup, one workgroup
