@@ -42,12 +42,14 @@
 // Softmax without rescaling.  The accumulators are never rescaled.  Each
 // row's reference max m is fixed by the first 32-key block of a segment and
 // p = 2^(s - m) is accumulated as is: numerator and denominator share m, so
-// the softmax is unchanged.  Later keys may score above m; this is safe while
-// p stays far inside the fp32 range.  Since every p >= 0, a lane's running
-// sum bounds each of its p, so one check per segment suffices: if a lane's
-// sum exceeds 2^headroom (32 by default) or an accumulator is not finite, the
-// segment is redone exactly -- a max-only sweep, then accumulation against
-// the true max.
+// the softmax is unchanged.  After that first block the score MFMAs start
+// from -m instead of 0 and deliver s - m themselves (one subtraction per
+// score less on the score wavefront).  Later keys may score above m; this is
+// safe while p stays far inside the fp32 range.  Since every p >= 0, a lane's
+// running sum bounds each of its p, so one check per segment suffices: if a
+// lane's sum exceeds 2^headroom (32 by default) or an accumulator is not
+// finite, the segment is redone exactly -- a max-only sweep, then
+// accumulation against the true max.
 #include "mla_common.h"
 #include "mla_kernels.h"
 
@@ -174,7 +176,17 @@ struct ScoreState {
   bf16x8 qf[NQB][AttendTile<DC>::KS];   // absorbed queries of the wavefront's halves (MFMA B operands)
   float m_ref[NQB];                     // reference max (base 2), identical in lanes l and l^32
   float l_run[NQB];                     // this lane's part of the running sum
+  f32x16 neg_m[NQB];                    // -m in every element: the accumulator a block's products start from
 };
+
+// Accumulator start -m for every later block of a segment (m = 0 for a row
+// with no visible key, whose scores are all -inf).
+template <int DC>
+__device__ __forceinline__ void set_neg_m(ScoreState<DC>& st, int qb) {
+  const float m = st.m_ref[qb] == -INFINITY ? 0.f : st.m_ref[qb];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) st.neg_m[qb][v] = -m;
+}
 
 constexpr int kScorePrefetch = 4;     // score operand loads in flight ahead of their MFMAs
 
@@ -183,8 +195,12 @@ constexpr int kScorePrefetch = 4;     // score operand loads in flight ahead of 
 // unmasked form has no masking branch after its products, so the scores
 // stay in the registers the products wrote (a branch that may rewrite them
 // made the compiler copy all 32 after every tile's second block).
-template <int DC, Pass P, bool MASK>
-__device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile, char* pbuf, int t, bool first_tile,
+// FIRST: the segment's first tile in a single-pass sweep; its first block
+// sets the reference max.  Every other block of a pass that accumulates
+// starts its products from -m, so the MFMAs deliver s - m and the softmax
+// takes 2^x of the accumulator directly.
+template <int DC, Pass P, bool MASK, bool FIRST>
+__device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile, char* pbuf, int t,
                                            const SweepCtx& c) {
   using L = AttendTile<DC>;
   constexpr int KS = L::KS, PF = kScorePrefetch, NQB = ScoreState<DC>::NQB;
@@ -201,9 +217,11 @@ __device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile,
 #pragma unroll
   for (int kb = 0; kb < L::NBLK; ++kb) {
     if (MASK && kb > 0 && kb * 32 >= left) break;
+    // fresh: the products start from 0 (the max pass, and the block that sets m)
+    const bool fresh = P == Pass::kMax || (FIRST && kb == 0);
     f32x16 s[NQB];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) s[qb] = f32x16{};
+    for (int qb = 0; qb < NQB; ++qb) s[qb] = fresh ? f32x16{} : st.neg_m[qb];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int g = kb * KS + ks;
@@ -238,12 +256,17 @@ __device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile,
         st.m_ref[qb] = fmaxf(st.m_ref[qb], block_max(s[qb]));
         continue;
       }
-      if (P == Pass::kSingle && first_tile && kb == 0) st.m_ref[qb] = block_max(s[qb]);
-      // a row with no visible key in this segment keeps m = -inf and p = 0
-      const float m = st.m_ref[qb] == -INFINITY ? 0.f : st.m_ref[qb];
       float p[16];
+      if (fresh) {
+        // a row with no visible key in this segment keeps m = -inf and p = 0
+        st.m_ref[qb] = block_max(s[qb]);
+        set_neg_m(st, qb);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(s[qb][v] - m);
+        for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(s[qb][v] + st.neg_m[qb][v]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(s[qb][v]);
+      }
       float q[8];
 #pragma unroll
       for (int v = 0; v < 8; ++v) q[v] = p[2 * v] + p[2 * v + 1];
@@ -316,7 +339,7 @@ __device__ __forceinline__ void value_tile(ValueState<DC>& st, const char* tile,
 // work (score: tile k in `cur`, P to P[k % 2]; value: tile k-1 in `prv`, P
 // from P[(k-1) % 2]), then wait for the loads and barrier.  Steps run
 // k = 0 .. n (n tiles); returns true after step n.
-template <int DC, Pass P, bool SCORE, class State>
+template <int DC, Pass P, bool SCORE, bool FIRST, class State>
 __device__ __forceinline__ bool sweep_step(State& st, int k, int n, int t0, char* cur, char* nxt, char* prv,
                                            char* pbuf, const SweepCtx& c) {
   if (!SCORE && k + 1 < n) issue_tile<DC>(c, t0 + k + 1, nxt);
@@ -325,10 +348,11 @@ __device__ __forceinline__ bool sweep_step(State& st, int k, int n, int t0, char
       constexpr int BN = AttendTile<DC>::BN;
       const int t = t0 + k;
       char* pb = pbuf + ((k & 1) ? AttendTile<DC>::PBUF : 0);
+      constexpr bool F = FIRST && P == Pass::kSingle;
       if (c.causal ? t * BN + BN > c.kv_min : c.n_k - t * BN < BN)
-        score_tile<DC, P, true>(st, cur, pb, t, k == 0, c);
+        score_tile<DC, P, true, F>(st, cur, pb, t, c);
       else
-        score_tile<DC, P, false>(st, cur, pb, t, k == 0, c);
+        score_tile<DC, P, false, F>(st, cur, pb, t, c);
     }
   } else {
     if (P != Pass::kMax && k >= 1) value_tile<DC>(st, prv, pbuf + ((k & 1) ? 0 : AttendTile<DC>::PBUF), t0 + k - 1, c);
@@ -342,6 +366,7 @@ __device__ __forceinline__ bool sweep_step(State& st, int k, int n, int t0, char
 // objects and each step names them statically (the loop is unrolled by
 // three), so reads of one are not ordered behind the in-flight direct loads
 // of another.  Score and value wavefronts run the same steps and barriers.
+// Step 0 (the segment's first tile) is peeled off the loop.
 template <int DC, Pass P, bool SCORE, class State>
 __device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* k2, char* pbuf, int t0, int t1,
                                       const SweepCtx& c) {
@@ -349,11 +374,12 @@ __device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* k2, c
   if (!SCORE) issue_tile<DC>(c, t0, k0);
   wait_vmcnt0();
   __syncthreads();
+  if (sweep_step<DC, P, SCORE, true>(st, 0, n, t0, k0, k1, k2, pbuf, c)) return;
 #pragma unroll 1
-  for (int k = 0;; k += 3) {
-    if (sweep_step<DC, P, SCORE>(st, k, n, t0, k0, k1, k2, pbuf, c)) break;
-    if (sweep_step<DC, P, SCORE>(st, k + 1, n, t0, k1, k2, k0, pbuf, c)) break;
-    if (sweep_step<DC, P, SCORE>(st, k + 2, n, t0, k2, k0, k1, pbuf, c)) break;
+  for (int k = 1;; k += 3) {
+    if (sweep_step<DC, P, SCORE, false>(st, k, n, t0, k1, k2, k0, pbuf, c)) break;
+    if (sweep_step<DC, P, SCORE, false>(st, k + 1, n, t0, k2, k0, k1, pbuf, c)) break;
+    if (sweep_step<DC, P, SCORE, false>(st, k + 2, n, t0, k0, k1, k2, pbuf, c)) break;
   }
 }
 
@@ -459,7 +485,10 @@ __device__ __forceinline__ void score_role(SweepCtx& c, SegmentIter it, const u1
       for (int qb = 0; qb < NQB; ++qb) st.m_ref[qb] = -INFINITY;
       sweep<DC, Pass::kMax, true>(st, k0, k1, k2, pbuf, it.t0, te, c);
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) st.l_run[qb] = 0.f;
+      for (int qb = 0; qb < NQB; ++qb) {
+        st.l_run[qb] = 0.f;
+        set_neg_m(st, qb);
+      }
       sweep<DC, Pass::kAccum, true>(st, k0, k1, k2, pbuf, it.t0, te, c);
     }
     const int64_t slot = seg_slot(w, it.rb);
