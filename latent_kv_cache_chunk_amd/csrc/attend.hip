@@ -188,7 +188,10 @@ __device__ __forceinline__ void set_neg_m(ScoreState<DC>& st, int qb) {
   for (int v = 0; v < 16; ++v) st.neg_m[qb][v] = -m;
 }
 
-constexpr int kScorePrefetch = 4;     // score operand loads in flight ahead of their MFMAs
+// Score operand loads in flight ahead of their MFMAs.  Six at d_c = 64 and
+// 192 (against four: 480P attention -0.6%, d_c = 64 -1.2%); four at d_c = 128,
+// where six was 0.5% slower.
+template <int DC> constexpr int score_prefetch() { return DC == 128 ? 4 : 6; }
 
 // Scores, softmax and P of every block of tile t (LDS `tile`), P to `pbuf`.
 // MASK: some key of the tile is past n_k or past a row's visible keys.  The
@@ -203,7 +206,7 @@ template <int DC, Pass P, bool MASK, bool FIRST>
 __device__ __forceinline__ void score_tile(ScoreState<DC>& st, const char* tile, char* pbuf, int t,
                                            const SweepCtx& c) {
   using L = AttendTile<DC>;
-  constexpr int KS = L::KS, PF = kScorePrefetch, NQB = ScoreState<DC>::NQB;
+  constexpr int KS = L::KS, PF = score_prefetch<DC>(), NQB = ScoreState<DC>::NQB;
   const int left = c.n_k - t * L::BN;
   // One stream of K operand reads over the tile's blocks: read g (block g /
   // KS, k-step g % KS) goes to slot g % PF and is issued PF k-steps ahead of
