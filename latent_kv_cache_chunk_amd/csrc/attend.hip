@@ -33,11 +33,13 @@
 // of the value wavefront unchanged.
 //
 // Pipeline.  Key tiles are copied global -> LDS by direct-to-LDS 16-byte
-// loads (no registers), one row per key padded to an odd number of 16-byte
-// slots so b128 reads of 16 consecutive rows hit distinct banks.  In step k
-// the score wavefronts work on tile k, the value wavefronts on tile k-1 (with
-// the P of step k-1), and tile k+1 is in flight (its loads issued by the
-// value wavefronts): three key buffers, two P buffers, one barrier per step.
+// loads (no registers; buffer loads at d_c >= 128, global ones at d_c = 64,
+// whichever measured faster), one row per key padded to an odd number of
+// 16-byte slots so b128 reads of 16 consecutive rows hit distinct banks.  In
+// step k the score wavefronts work on tile k, the value wavefronts on tile
+// k-1 (with the P of step k-1), and tile k+1 is in flight (its loads issued
+// by the value wavefronts): three key buffers, two P buffers, one barrier per
+// step.
 //
 // Softmax without rescaling.  The accumulators are never rescaled.  Each
 // row's reference max m is fixed by the first 32-key block of a segment and
@@ -105,7 +107,8 @@ __device__ inline int lane_copy_chunk(int lane, int& lane_row) {
 
 // Wave-invariant addressing of one sweep.
 struct SweepCtx {
-  const char* gbase;   // cache rows of this sample
+  const char* gbase;             // cache rows of this sample
+  __amdgpu_buffer_rsrc_t gsrc;   // buffer resource over the visible cache rows of this sample
   int n_k;
   bool causal;         // keys limited per row (chunk-causal visibility)
   int kv[2];           // score lanes: visible keys of the lane's row in each of the wavefront's halves
@@ -117,6 +120,23 @@ struct SweepCtx {
   int v_off;           // transposed latent operand offset inside a block
 };
 
+// Buffer resource over rows [0, n_k) of sample b.  At d_c >= 128 the tiles
+// are copied by buffer loads to LDS rather than global ones: after a global
+// load to LDS the compiler must assume the load may still touch LDS out of
+// order, so every wait on this wavefront's own LDS reads became a wait for
+// all of them (lgkmcnt(0)) until the next wait for vector memory.  Traced
+// attention with buffer loads: 480P -0.4%, d_c = 128 -0.4%, block-causal
+// -2.3%, but d_c = 64 +1.2%, which keeps global loads.
+template <int DC> constexpr bool buffer_tile_loads() { return DC >= 128; }
+template <int DC>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sample_rows(const u16* cache, int64_t cache_bstride, int b,
+                                                              int n_k) {
+  // byte count below 4 GiB (checked by the host), the hardware reads it unsigned
+  const uint32_t bytes = (uint32_t)n_k * (uint32_t)(AttendTile<DC>::W * 2);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(cache + (int64_t)b * cache_bstride), 0, (int)bytes,
+                                           0x00020000);
+}
+
 // Enqueue this value wavefront's share of the direct-to-LDS loads of key tile
 // t into `tile`.  Only the value wavefronts issue loads: the score wavefront
 // is each step's critical path (its scores, softmax and P stores take longer
@@ -124,7 +144,8 @@ struct SweepCtx {
 // step.  Load i copies R = ROWS_PER_LOAD whole rows, [iR, iR + R), to
 // LDS rows [iR, iR + R); in the last, partial tile rows past n_k re-read key
 // n_k-1 (their scores are masked).  Source addresses are the sample's base
-// plus a 32-bit unsigned offset (a sample's cache is below 4 GiB).
+// plus a 32-bit unsigned offset (a sample's cache is below 4 GiB), inside the
+// buffer resource's n_k rows.
 template <int DC>
 __device__ inline void issue_tile(const SweepCtx& c, int t, char* tile) {
   using L = AttendTile<DC>;
@@ -136,8 +157,12 @@ __device__ inline void issue_tile(const SweepCtx& c, int t, char* tile) {
       const int row0 = ld * L::ROWS_PER_LOAD;
       const uint32_t key = (uint32_t)min(key0 + row0 + c.lane_row, c.n_k - 1);
       const uint32_t off = key * (uint32_t)(L::W * 2) + (uint32_t)c.lane_chunk;
-      if (c.lane_row < L::ROWS_PER_LOAD && row0 + c.lane_row < L::BN)
-        __builtin_amdgcn_global_load_lds(c.gbase + off, (lds_void*)(tile + row0 * L::ROWB), 16, 0, 0);
+      if (c.lane_row < L::ROWS_PER_LOAD && row0 + c.lane_row < L::BN) {
+        if constexpr (buffer_tile_loads<DC>())
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(c.gsrc, (lds_void*)(tile + row0 * L::ROWB), 16, off, 0, 0, 0);
+        else
+          __builtin_amdgcn_global_load_lds(c.gbase + off, (lds_void*)(tile + row0 * L::ROWB), 16, 0, 0);
+      }
     }
   }
 }
@@ -464,6 +489,7 @@ __device__ __forceinline__ void score_role(SweepCtx& c, SegmentIter it, const u1
   int parity = 0;
   while (it.next()) {
     c.gbase = reinterpret_cast<const char*>(cache + (int64_t)it.b * cache_bstride);
+    c.gsrc = sample_rows<DC>(cache, cache_bstride, it.b, c.n_k);
     const int te = visible_end<DC>(it, vis, c.n_k);
     const int64_t row0 = (int64_t)it.b * rows_pad_b + (int64_t)it.rbl * kRowsPerBlock + c.group * kGroupRows;
 #pragma unroll
@@ -517,6 +543,7 @@ __device__ __forceinline__ void value_role(SweepCtx& c, SegmentIter it, const u1
   int parity = 0;
   while (it.next()) {
     c.gbase = reinterpret_cast<const char*>(cache + (int64_t)it.b * cache_bstride);
+    c.gsrc = sample_rows<DC>(cache, cache_bstride, it.b, c.n_k);
     const int te = visible_end<DC>(it, vis, c.n_k);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)

@@ -21,8 +21,8 @@
 // exactly those keys for the P.V k-step, so P never moves between lanes.
 //
 // Staging: each tile of key_tile(256) keys is copied global -> LDS by
-// direct-to-LDS 16-byte loads (no registers), one row per key padded to an
-// odd number of 16-byte slots so b128 reads of 16 consecutive rows hit
+// direct-to-LDS 16-byte buffer loads (no registers), one row per key padded
+// to an odd number of 16-byte slots so b128 reads of 16 consecutive rows hit
 // distinct banks.  Two buffers: the next tile's loads are in flight while the
 // current one is used; one barrier per tile.
 //
@@ -78,7 +78,7 @@ __device__ inline int lane_copy_offset(int lane, int& lane_row) {
 // [iR, iR + R); in the last, partial tile rows past n_k re-read key n_k-1
 // (their scores are masked).
 template <int DC, int NW>
-__device__ inline void issue_tile(const char* gbase, int key0, int n_k, char* tile, int wave, int lane_off,
+__device__ inline void issue_tile(__amdgpu_buffer_rsrc_t gsrc, int key0, int n_k, char* tile, int wave, int lane_off,
                                   int lane_row) {
   using L = AttendTile<DC, NW>;
   const bool partial = key0 + L::BN > n_k;
@@ -87,14 +87,14 @@ __device__ inline void issue_tile(const char* gbase, int key0, int n_k, char* ti
     const int ld = wave + NW * i;
     if (ld < L::NLOAD) {
       const int row0 = ld * L::ROWS_PER_LOAD;
-      const char* src = gbase + (int64_t)(key0 + row0) * (L::W * 2);
+      const uint32_t src = (uint32_t)(key0 + row0) * (uint32_t)(L::W * 2);
       int o = lane_off;
       if (partial) {
         const int key = key0 + row0 + lane_row;
         o += (min(key, n_k - 1) - key) * (L::W * 2);
       }
       if (lane_row < L::ROWS_PER_LOAD && row0 + lane_row < L::BN)
-        __builtin_amdgcn_global_load_lds(src + o, (lds_void*)(tile + row0 * L::ROWB), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(gsrc, (lds_void*)(tile + row0 * L::ROWB), 16, src + (uint32_t)o, 0, 0, 0);
     }
   }
 }
@@ -278,24 +278,24 @@ __device__ __forceinline__ void attend_tile(WaveState<DC, QB>& st, const char* t
 // identically in every wave, if some lane's running sum rose above
 // 2^headroom or some accumulator is not finite.
 template <int DC, int QB, int NW, Pass P>
-__device__ __forceinline__ bool sweep(WaveState<DC, QB>& st, char* sbuf0, char* sbuf1, const char* gbase, int t0,
+__device__ __forceinline__ bool sweep(WaveState<DC, QB>& st, char* sbuf0, char* sbuf1, __amdgpu_buffer_rsrc_t gsrc, int t0,
                                       int t1, int n_k, int wave, int lane_off, int lane_row, int s_off, int v_off,
                                       int half, float headroom) {
   using L = AttendTile<DC, NW>;
   constexpr int BN = L::BN;
   bool over = false;
-  issue_tile<DC, NW>(gbase, t0 * BN, n_k, sbuf0, wave, lane_off, lane_row);
+  issue_tile<DC, NW>(gsrc, t0 * BN, n_k, sbuf0, wave, lane_off, lane_row);
   wait_vmcnt0();
   __syncthreads();
 #pragma unroll 1
   for (int t = t0; t < t1; t += 2) {
     // tile t is in sbuf0; tile t+1 goes to sbuf1
-    if (t + 1 < t1) issue_tile<DC, NW>(gbase, (t + 1) * BN, n_k, sbuf1, wave, lane_off, lane_row);
+    if (t + 1 < t1) issue_tile<DC, NW>(gsrc, (t + 1) * BN, n_k, sbuf1, wave, lane_off, lane_row);
     attend_tile<DC, QB, NW, P>(st, sbuf0, t * BN, n_k - t * BN, s_off, v_off, half, t == t0, headroom, over);
     wait_vmcnt0();
     __syncthreads();
     if (t + 1 >= t1) break;
-    if (t + 2 < t1) issue_tile<DC, NW>(gbase, (t + 2) * BN, n_k, sbuf0, wave, lane_off, lane_row);
+    if (t + 2 < t1) issue_tile<DC, NW>(gsrc, (t + 2) * BN, n_k, sbuf0, wave, lane_off, lane_row);
     attend_tile<DC, QB, NW, P>(st, sbuf1, (t + 1) * BN, n_k - (t + 1) * BN, s_off, v_off, half, false, headroom, over);
     wait_vmcnt0();
     __syncthreads();
@@ -378,7 +378,15 @@ void attend_wide_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstrid
     }
     const int b = (int)(rb / rb_per_b);
     const int rbl = (int)(rb - (int64_t)b * rb_per_b);
-    const char* gbase = reinterpret_cast<const char*>(cache + (int64_t)b * cache_bstride);
+    // Buffer resource over the sample's n_k rows (a byte count below 4 GiB,
+    // checked by the host; the hardware reads it unsigned).  Tiles are copied
+    // by buffer loads to LDS rather than global ones: after a global load to
+    // LDS the compiler must assume the load may still touch LDS out of order,
+    // so every wait on this wavefront's own LDS reads became a wait for all of
+    // them (lgkmcnt(0)).  Traced attention at d_c = 256: -4.1%.
+    const __amdgpu_buffer_rsrc_t gsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u16*>(cache + (int64_t)b * cache_bstride), 0, (int)((uint32_t)n_k * (uint32_t)(W * 2)),
+        0x00020000);
 
     {
       const int64_t row0 = (int64_t)b * rows_pad_b + (int64_t)rbl * kRowsPerBlock + wave * 32 * QB;
@@ -403,16 +411,16 @@ void attend_wide_bf16_kernel(const u16* __restrict__ cache, int64_t cache_bstrid
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) kvm = min(kvm, __shfl_xor(kvm, o));
     st.kv_min = kvm;
-    if (te > t0 && sweep<DC, QB, NW, Pass::kSingle>(st, sbuf0, sbuf1, gbase, t0, te, n_k, wave, lane_off, lane_row,
+    if (te > t0 && sweep<DC, QB, NW, Pass::kSingle>(st, sbuf0, sbuf1, gsrc, t0, te, n_k, wave, lane_off, lane_row,
                                                     s_off, v_off, half, headroom)) {
       // A lane's running sum rose above 2^headroom (or an accumulator is not finite):
       // exact two-pass evaluation of this segment.
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) st.m_ref[qb] = -INFINITY;
-      sweep<DC, QB, NW, Pass::kMax>(st, sbuf0, sbuf1, gbase, t0, te, n_k, wave, lane_off, lane_row, s_off, v_off,
+      sweep<DC, QB, NW, Pass::kMax>(st, sbuf0, sbuf1, gsrc, t0, te, n_k, wave, lane_off, lane_row, s_off, v_off,
                                     half, headroom);
       reset_acc<DC, QB>(st);
-      sweep<DC, QB, NW, Pass::kAccum>(st, sbuf0, sbuf1, gbase, t0, te, n_k, wave, lane_off, lane_row, s_off,
+      sweep<DC, QB, NW, Pass::kAccum>(st, sbuf0, sbuf1, gsrc, t0, te, n_k, wave, lane_off, lane_row, s_off,
                                       v_off, half, headroom);
     }
 
