@@ -79,8 +79,8 @@ __device__ inline LaneCopy lane_copy(int lane) {
 }
 
 struct Ctx {
-  const char* kbase;     // key 0 of this (batch, head) in K
-  const char* vbase;     // key 0 of this (batch, head) in V
+  __amdgpu_buffer_rsrc_t ksrc;   // buffer resource over the n_k keys of this (batch, head) in K
+  __amdgpu_buffer_rsrc_t vsrc;   // and in V
   uint32_t krow, vrow;   // bytes between consecutive keys in K and V
   LaneCopy kc, vc;
   int n_k;
@@ -92,10 +92,13 @@ struct Ctx {
 // of one tensor (the score wavefronts, each step's critical path, issue
 // none): load ld copies rows [ld*ROWS, ld*ROWS + ROWS).  Keys past n_k
 // re-read key n_k - 1 (their scores are masked).  Offsets are 32-bit: one
-// (batch, head)'s keys span less than 4 GiB.
+// (batch, head)'s keys span less than 4 GiB.  The copies are buffer loads to
+// LDS: after a global load to LDS the compiler must assume the load may still
+// touch LDS out of order, and every wait on this wavefront's own LDS reads
+// became a wait for all of them.
 template <int D>
-__device__ inline void issue_rows(const Ctx& c, const char* base, uint32_t row_bytes, const LaneCopy& lc, int t,
-                                  char* buf) {
+__device__ inline void issue_rows(const Ctx& c, __amdgpu_buffer_rsrc_t src, uint32_t row_bytes, const LaneCopy& lc,
+                                  int t, char* buf) {
   using R = Rows<D>;
 #pragma unroll
   for (int i = 0; i < R::PER_WAVE; ++i) {
@@ -104,8 +107,8 @@ __device__ inline void issue_rows(const Ctx& c, const char* base, uint32_t row_b
       const int row0 = ld * R::ROWS;
       const uint32_t key = (uint32_t)min(t * kBN + row0 + lc.row, c.n_k - 1);
       if (lc.row < R::ROWS && row0 + lc.row < kBN)
-        __builtin_amdgcn_global_load_lds(base + (key * row_bytes + lc.chunk), (lds_void*)(buf + row0 * R::ROWB), 16,
-                                         0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)(buf + row0 * R::ROWB), 16, key * row_bytes + lc.chunk,
+                                                 0, 0, 0);
     }
   }
 }
@@ -254,8 +257,8 @@ __device__ __forceinline__ void value_tile(ValueState& st, const char* vbuf, con
 template <int DQK, Pass P, bool SCORE, class State>
 __device__ __forceinline__ bool sweep_step(State& st, int k, int n, int t0, char* kcur, char* knxt, char* vload,
                                            char* vprev, char* pcur, char* pprev, const Ctx& c) {
-  if (!SCORE && k + 1 < n) issue_rows<DQK>(c, c.kbase, c.krow, c.kc, t0 + k + 1, knxt);
-  if (!SCORE && P != Pass::kMax && k < n) issue_rows<kDV>(c, c.vbase, c.vrow, c.vc, t0 + k, vload);
+  if (!SCORE && k + 1 < n) issue_rows<DQK>(c, c.ksrc, c.krow, c.kc, t0 + k + 1, knxt);
+  if (!SCORE && P != Pass::kMax && k < n) issue_rows<kDV>(c, c.vsrc, c.vrow, c.vc, t0 + k, vload);
   if constexpr (SCORE) {
     if (k < n) score_tile<DQK, P>(st, kcur, pcur, t0 + k, k == 0, c);
   } else {
@@ -270,7 +273,7 @@ template <int DQK, Pass P, bool SCORE, class State>
 __device__ __forceinline__ void sweep(State& st, char* k0, char* k1, char* v0, char* v1, char* pb0, char* pb1,
                                       int t0, int t1, const Ctx& c) {
   const int n = t1 - t0;
-  if (!SCORE) issue_rows<DQK>(c, c.kbase, c.krow, c.kc, t0, k0);
+  if (!SCORE) issue_rows<DQK>(c, c.ksrc, c.krow, c.kc, t0, k0);
   wait_vmcnt0();
   __syncthreads();
 #pragma unroll 1
@@ -302,8 +305,10 @@ __device__ __forceinline__ void begin_segment(Ctx& c, const Problem& pr, int64_t
   const int b = (int)(bh / pr.H), h = (int)(bh - (int64_t)b * pr.H);
   // row (of DQK or kDV elements) of key 0 of this (batch, head)
   const int64_t tok0 = pr.head_major ? ((int64_t)b * pr.H + h) * pr.cap : (int64_t)b * pr.cap * pr.H + h;
-  c.kbase = reinterpret_cast<const char*>(pr.k + tok0 * DQK);
-  c.vbase = reinterpret_cast<const char*>(pr.v + tok0 * kDV);
+  // bytes from key 0 to the end of key n_k - 1 (below 4 GiB; read unsigned)
+  const uint32_t kbytes = (uint32_t)(pr.n_k - 1) * c.krow + DQK * 2, vbytes = (uint32_t)(pr.n_k - 1) * c.vrow + kDV * 2;
+  c.ksrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(pr.k + tok0 * DQK), 0, (int)kbytes, 0x00020000);
+  c.vsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(pr.v + tok0 * kDV), 0, (int)vbytes, 0x00020000);
 }
 
 template <int DQK, bool SCORE>
