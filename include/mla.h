@@ -258,10 +258,10 @@ int32_t mla_chunk_attend_expanded(const mla_dims* dims, int32_t out_dtype,
 
 /* The faster of the two evaluation orders for a chunk step's shape, picked
  * from measured times on MI355X: MLA_FORM_EXPANDED (mla_chunk_attend_expanded)
- * when in_dtype is MLA_BF16 and n_q >= 1152 at d_c = 192 or n_q >= 448 at
+ * when in_dtype is MLA_BF16 and n_q >= 1280 at d_c = 192 or n_q >= 448 at
  * d_c = 256 (and the per-head keys fit its limits); otherwise
  * MLA_FORM_ABSORBED (mla_chunk_attend).  At the 480P shape (d_c = 192, 4680
- * queries, 32760 keys) the non-absorbed form is about 15% faster; at d_c <=
+ * queries, 32760 keys) the non-absorbed form is about 13% faster; at d_c <=
  * 128 the absorbed form always is.  Negative mla_status on arguments
  * mla_chunk_attend would reject. */
 enum { MLA_FORM_ABSORBED = 0, MLA_FORM_EXPANDED = 1 };

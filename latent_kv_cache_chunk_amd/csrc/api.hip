@@ -422,10 +422,11 @@ int32_t mla_chunk_attend_form(const mla_dims* dims, int32_t in_dtype, int32_t n_
   int32_t st = check_attend_sizes(dims, in_dtype, n_q, n_k, &p);
   if (st) return st;
   // Thresholds from timing both forms on MI355X (n_k = 32760; d_c 64-256):
-  // the non-absorbed form wins at d_c = 192 from about 1152 queries per chunk
-  // (the two are level at 1024) and at d_c = 256 from about 448 (absorbed
-  // faster at 384, slower at 520); at d_c <= 128 the absorbed form always.
-  const int32_t from = dims->d_c >= 256 ? 448 : dims->d_c >= 192 ? 1152 : INT32_MAX;
+  // the non-absorbed form wins at d_c = 192 from about 1280 queries per chunk
+  // (absorbed 2% faster at 1152, 3% slower at 1280) and at d_c = 256 from
+  // about 448 (level at 384, absorbed 8% slower at 448); at d_c <= 128 the
+  // absorbed form always.
+  const int32_t from = dims->d_c >= 256 ? 448 : dims->d_c >= 192 ? 1280 : INT32_MAX;
   if (in_dtype != MLA_BF16 || n_q < from) return MLA_FORM_ABSORBED;
   if (check_mha_sizes(dims->batch, dims->n_heads, n_q, n_k, 160) ||
       (int64_t)n_k * dims->n_heads * 160 * 2 >= (int64_t)1 << 32)

@@ -208,8 +208,8 @@ def test_chunk_attend_form_rule():
     d192 = _dims()
     assert form(d192, 0, 4680) == 1                     # 480P chunk: non-absorbed (4864 rows per head)
     assert form(d192, 0, 1560) == 1
-    assert form(d192, 0, 1151) == 0                     # below 1152 queries at d_c = 192
-    assert form(d192, 0, 1152) == 1
+    assert form(d192, 0, 1279) == 0                     # below 1280 queries at d_c = 192
+    assert form(d192, 0, 1280) == 1
     assert form(d192, 1, 4680) == 0                     # fp32 inputs: absorbed only
     assert form(_dims(d_c=128), 0, 4680) == 0           # d_c <= 128: absorbed at every size
     assert form(_dims(d_c=256), 0, 4680) == 1
