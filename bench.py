@@ -354,6 +354,12 @@ def main(argv=None) -> int:
                                  f"({wl.batch * wl.n_q * wl.n_heads} rows, {wl.n_k} keys)"},
         "cpu_baseline": None,
         "library": library_identity(mla.LIB_PATH),
+        # The pages' only speed figures: whole-pipeline generation rates on another GPU, for context.
+        # They time a full model, not this step, so vs_baseline stays null.
+        "context": {"pages_generation_fps": {"latent_cache": 23.96, "per_head_cache_baseline": 18.06},
+                    "pages_speedup_claim": 1.23,
+                    "setting": "batch 1, whole autoregressive video generation pipeline, one NVIDIA B200; "
+                               "not comparable to this kernel-level step"},
     }
     if not args.no_compare and not wl.causal:
         res["comparison"] = compare(wl, dims, t, absorb_ms + attend_ms + upproj_ms, args.seed, dev)
